@@ -1,0 +1,229 @@
+"""CPU oracle for exact attention forward (fp64) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package.  It shares no code with the GPU
+library (``exact_attention_95_amd``) and never imports it.
+
+The arithmetic lives in ``fa_oracle.c`` (plain C, IEEE double, libm); this
+module only builds that file with gcc, converts inputs to float64 one
+(batch, head) slice at a time and calls it through ctypes.
+
+Functions and the passages they follow:
+
+* :func:`attention` -- standard attention, three-pass softmax per row
+  ("FlashAttention算子优化" section 1; plate 04 of "FlashAttention 与显存";
+  section 1.3 of "Flash Attention 原理与实践").
+* :func:`attention_blockwise` -- blockwise online softmax in v2 order
+  ("FlashAttention算子优化" section 2, merge rule of plate 08) or v1 order
+  ("Flash Attention 原理与实践" section 2.3).
+* :func:`dequant_e4m3` -- OCP E4M3 code times a per-tensor descale.
+
+Pins (tests/test_oracle.py): brute force at 50 digits with mpmath, the
+unshifted textbook softmax, scipy's logsumexp, closed forms (one key, two
+keys, Q = 0, constant V, shifted V, equal keys, causal row 0), rows of P
+summing to 1, blockwise == naive on random partitions and tile shapes,
+v1 == v2, planted mistakes caught, and the E4M3 decoder against torch's
+float8_e4m3fn.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compiles the oracle's C source into a shared library with gcc."""
+    if (not force and os.path.exists(out)
+            and os.path.getmtime(out) >= os.path.getmtime(src)):
+        return out
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Loads (building first if needed) and returns the ctypes library."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            _lib = _declare(ctypes.CDLL(build()))
+        return _lib
+
+
+def _declare(lib):
+    lib.fa_oracle_naive.restype = ctypes.c_int
+    lib.fa_oracle_naive.argtypes = [
+        _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+        ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64, _dp, _dp, _dp]
+    for name in ("fa_oracle_blockwise", "fa_oracle_blockwise_v1"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [
+            _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64, _i64p,
+            ctypes.c_int64, _dp, _dp]
+    lib.fa_oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.fa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.fa_oracle_dequant_e4m3.restype = ctypes.c_int
+    lib.fa_oracle_dequant_e4m3.argtypes = [
+        ctypes.POINTER(ctypes.c_uint8), ctypes.c_int64, ctypes.c_double, _dp]
+    return lib
+
+
+def _ptr(a, typ=_dp):
+    return a.ctypes.data_as(typ) if a is not None else None
+
+
+def _as_f64(x) -> np.ndarray:
+    """float64 copy of a numpy array or CPU torch tensor (exact for fp16/bf16/fp32)."""
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _heads(x):
+    """Views [B,H,N,d] (or [N,d]) as a list of per-head 2-D slices."""
+    if x.ndim == 2:
+        return x[None, None]
+    if x.ndim != 4:
+        raise ValueError("expected [B,H,N,d] or [N,d]")
+    return x
+
+
+def attention(q, k, v, scale: float, causal: bool = False, rows=None,
+              return_p: bool = False, lib=None):
+    """Standard attention in fp64 (three-pass softmax per row).
+
+    q: [B,H,N_q,d], k and v: [B,H,N_kv,d] (numpy or CPU torch, any float
+    dtype; converted exactly to float64 one head at a time).  ``scale`` is
+    applied to the scores before the max; pass the same value the GPU
+    library receives (e.g. the float32 nearest to 1/sqrt(d)).
+    ``rows``: optional int array of flat row indices into B*H*N_q; then the
+    results are [len(rows), d] and [len(rows)].  Otherwise O is
+    [B,H,N_q,d] and LSE [B,H,N_q].  ``return_p`` adds P ([..., N_kv]).
+    """
+    lib = lib or load()
+    q4, k4, v4 = (_heads(t) for t in (q, k, v))
+    B, H, n_q, d = q4.shape
+    n_kv = k4.shape[2]
+    if k4.shape != (B, H, n_kv, d) or v4.shape != (B, H, n_kv, d):
+        raise ValueError("shape mismatch")
+    if rows is None:
+        o = np.empty((B, H, n_q, d))
+        lse = np.empty((B, H, n_q))
+        p = np.empty((B, H, n_q, n_kv)) if return_p else None
+        for b in range(B):
+            for h in range(H):
+                qh, kh, vh = _as_f64(q4[b, h]), _as_f64(k4[b, h]), _as_f64(v4[b, h])
+                oh = np.empty((n_q, d))
+                lh = np.empty(n_q)
+                ph = np.empty((n_q, n_kv)) if return_p else None
+                st = lib.fa_oracle_naive(_ptr(qh), _ptr(kh), _ptr(vh), n_q, n_kv, d,
+                                         float(scale), int(bool(causal)), None, n_q,
+                                         _ptr(oh), _ptr(lh), _ptr(ph))
+                if st:
+                    raise RuntimeError("fa_oracle_naive failed: %d" % st)
+                o[b, h], lse[b, h] = oh, lh
+                if return_p:
+                    p[b, h] = ph
+        if q.ndim == 2:
+            o, lse = o[0, 0], lse[0, 0]
+            p = p[0, 0] if return_p else None
+        return (o, lse, p) if return_p else (o, lse)
+    rows = np.asarray(rows, dtype=np.int64).ravel()
+    o = np.empty((rows.size, d))
+    lse = np.empty(rows.size)
+    p = np.empty((rows.size, n_kv)) if return_p else None
+    head_of = rows // n_q
+    for bh in np.unique(head_of):
+        sel = np.nonzero(head_of == bh)[0]
+        b, h = divmod(int(bh), H)
+        local = np.ascontiguousarray(rows[sel] - bh * n_q)
+        qh, kh, vh = _as_f64(q4[b, h]), _as_f64(k4[b, h]), _as_f64(v4[b, h])
+        oh = np.empty((sel.size, d))
+        lh = np.empty(sel.size)
+        ph = np.empty((sel.size, n_kv)) if return_p else None
+        st = lib.fa_oracle_naive(_ptr(qh), _ptr(kh), _ptr(vh), n_q, n_kv, d,
+                                 float(scale), int(bool(causal)), _ptr(local, _i64p),
+                                 sel.size, _ptr(oh), _ptr(lh), _ptr(ph))
+        if st:
+            raise RuntimeError("fa_oracle_naive failed: %d" % st)
+        o[sel], lse[sel] = oh, lh
+        if return_p:
+            p[sel] = ph
+    return (o, lse, p) if return_p else (o, lse)
+
+
+def cuts_from_block(n: int, block: int) -> np.ndarray:
+    """Boundaries of consecutive blocks of ``block`` rows, last one ragged."""
+    c = list(range(0, n, block)) + [n]
+    return np.asarray(c, dtype=np.int64)
+
+
+def attention_blockwise(q, k, v, scale: float, causal: bool = False,
+                        q_cuts=None, kv_cuts=None, br: int | None = None,
+                        bc: int | None = None, order: str = "v2", lib=None):
+    """Blockwise online-softmax attention for one head ([N,d] inputs).
+
+    Give the partitions as explicit boundaries (``q_cuts``/``kv_cuts``,
+    starting at 0 and ending at N) or as block sizes ``br``/``bc``.
+    ``order`` is "v2" (query block outside, division after the key loop) or
+    "v1" (key block outside, normalised O written back each step).
+    """
+    lib = lib or load()
+    qh, kh, vh = _as_f64(q), _as_f64(k), _as_f64(v)
+    n_q, d = qh.shape
+    n_kv = kh.shape[0]
+    if q_cuts is None:
+        q_cuts = cuts_from_block(n_q, br or n_q)
+    if kv_cuts is None:
+        kv_cuts = cuts_from_block(n_kv, bc or n_kv)
+    q_cuts = np.ascontiguousarray(q_cuts, dtype=np.int64)
+    kv_cuts = np.ascontiguousarray(kv_cuts, dtype=np.int64)
+    o = np.empty((n_q, d))
+    lse = np.empty(n_q)
+    fn = {"v2": lib.fa_oracle_blockwise, "v1": lib.fa_oracle_blockwise_v1}[order]
+    st = fn(_ptr(qh), _ptr(kh), _ptr(vh), n_q, n_kv, d, float(scale), int(bool(causal)),
+            _ptr(q_cuts, _i64p), q_cuts.size, _ptr(kv_cuts, _i64p), kv_cuts.size,
+            _ptr(o), _ptr(lse))
+    if st:
+        raise RuntimeError("blockwise oracle failed: %d" % st)
+    return o, lse
+
+
+def e4m3_to_double(code: int, lib=None) -> float:
+    """Value of one OCP E4M3 (fn) code."""
+    return (lib or load()).fa_oracle_e4m3_to_double(int(code) & 0xFF)
+
+
+def dequant_e4m3(codes, descale: float, lib=None) -> np.ndarray:
+    """E4M3 codes (uint8 array or torch float8_e4m3fn tensor) times descale, in fp64."""
+    lib = lib or load()
+    if hasattr(codes, "detach"):
+        import torch
+        codes = codes.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float64)
+    st = lib.fa_oracle_dequant_e4m3(c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                    c.size, float(descale), _ptr(out))
+    if st:
+        raise RuntimeError("dequant failed")
+    return out

@@ -1,0 +1,302 @@
+/*
+ * CPU oracle for exact scaled-dot-product attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no
+ * code, header, table or helper with the GPU library, and it never sees a
+ * value produced by the GPU library except to compare against it.
+ *
+ * Everything is computed in IEEE double precision with libm exp/log, in the
+ * plain order the method's definition gives, with no blocking or fusion
+ * beyond what each function's cited passage states.
+ *
+ * Sources (pages of the reference; sections as numbered on each page):
+ *  - "Flash Attention 原理与实践" (bjdmk.com.cn), section 1.3: standard
+ *    attention S = QK^T, P = softmax(S), O = PV; section 2.2: the online
+ *    softmax identity; section 2.3: the v1 loop order (KV outer, Q inner,
+ *    O/l/m written back after every step).
+ *  - "FlashAttention算子优化" (viperekura.xyz), section 1: the three-pass
+ *    softmax (row max, exp-sum, normalise); section 2: the fused forward in
+ *    v2 loop order (one Q block, KV blocks inside, division by l after the
+ *    KV loop), scale = 1/sqrt(d) applied to S before the max.
+ *  - "FlashAttention 与显存" (world.lapla.si plate F51), plate 04 (standard
+ *    method), plate 08 (merge rule m_new = max(m, m~),
+ *    l_new = e^(m - m_new) l + e^(m~ - m_new) l~, result equal to the
+ *    full-row softmax up to rounding), plate 09 (only O and per-row
+ *    statistics are kept).
+ *
+ * Readings where the pages are silent (each restated in the design notes):
+ *  - causal masking is top-left aligned: key j is visible to query i iff
+ *    j <= i (also when n_q != n_kv);
+ *  - LSE_i = m_i + ln(l_i) in natural-log units of the scaled scores;
+ *  - a key block with no visible key for a row is skipped for that row (the
+ *    merge would otherwise form e^(-inf - (-inf)));
+ *  - ragged tails: block counts use the ceiling and the last block is
+ *    shorter (the floor in the v1 listing would drop the tail).
+ *
+ * Status codes: 0 ok, 1 bad argument, 2 out of memory.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Number of keys row i may attend to. */
+static int64_t visible_keys(int64_t i, int64_t n_kv, int causal)
+{
+    if (!causal) return n_kv;
+    return (i + 1 < n_kv) ? i + 1 : n_kv;
+}
+
+/* s = scale * <q_i, k_j>, plain sequential dot product. */
+static double score(const double *qi, const double *kj, int64_t d, double scale)
+{
+    double acc = 0.0;
+    for (int64_t c = 0; c < d; ++c) acc += qi[c] * kj[c];
+    return scale * acc;
+}
+
+/*
+ * Standard attention for selected rows of one (batch, head) slice, in the
+ * three passes of the softmax ("FlashAttention算子优化" section 1; standard
+ * method of plate 04 and section 1.3 of the first page):
+ *   pass 1: s_j = scale * q_i . k_j for visible j, m = max_j s_j
+ *   pass 2: l = sum_j exp(s_j - m)
+ *   pass 3: P_ij = exp(s_j - m) / l, O_i = sum_j P_ij v_j
+ *   LSE_i = m + ln l
+ * q: [n_q, d], k, v: [n_kv, d], row-major.  rows: row indices into q (NULL =
+ * all n_q rows, then n_rows must equal n_q).  o: [n_rows, d], lse: [n_rows],
+ * p: optional [n_rows, n_kv] probabilities (masked entries 0).
+ */
+int fa_oracle_naive(const double *q, const double *k, const double *v,
+                    int64_t n_q, int64_t n_kv, int64_t d, double scale, int causal,
+                    const int64_t *rows, int64_t n_rows,
+                    double *o, double *lse, double *p)
+{
+    if (!q || !k || !v || !o || !lse || n_q < 0 || n_kv < 1 || d < 1 || n_rows < 0) return 1;
+    if (!rows && n_rows != n_q) return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= n_q) return 1;
+    }
+    int status = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)n_kv * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            status = 2;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (!s) continue;
+            int64_t i = rows ? rows[r] : r;
+            const double *qi = q + i * d;
+            int64_t nv = visible_keys(i, n_kv, causal);
+            /* pass 1 */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nv; ++j) {
+                s[j] = score(qi, k + j * d, d, scale);
+                if (s[j] > m) m = s[j];
+            }
+            /* pass 2 */
+            double l = 0.0;
+            for (int64_t j = 0; j < nv; ++j) l += exp(s[j] - m);
+            /* pass 3 */
+            double *oi = o + r * d;
+            for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+            for (int64_t j = 0; j < nv; ++j) {
+                double pij = exp(s[j] - m) / l;
+                if (p) p[r * n_kv + j] = pij;
+                const double *vj = v + j * d;
+                for (int64_t c = 0; c < d; ++c) oi[c] += pij * vj[c];
+            }
+            if (p)
+                for (int64_t j = nv; j < n_kv; ++j) p[r * n_kv + j] = 0.0;
+            lse[r] = m + log(l);
+        }
+        free(s);
+    }
+    return status;
+}
+
+/* Checks that cuts is 0 = c_0 < c_1 < ... < c_{n-1} = total. */
+static int valid_cuts(const int64_t *cuts, int64_t n, int64_t total)
+{
+    if (!cuts || n < 2 || cuts[0] != 0 || cuts[n - 1] != total) return 0;
+    for (int64_t t = 1; t < n; ++t)
+        if (cuts[t] <= cuts[t - 1]) return 0;
+    return 1;
+}
+
+/*
+ * Blockwise forward in v2 loop order ("FlashAttention算子优化" section 2):
+ * for each query block, a running (m, l, O_acc) per row starts at
+ * (-inf, 0, 0); each key block contributes its own block max m~, block
+ * probabilities P~ = exp(s - m~), block sum l~ = sum P~ and block product
+ * P~ V; they are merged with the rule of plate 08:
+ *   m_new = max(m, m~)
+ *   l     = e^(m - m_new) l + e^(m~ - m_new) l~
+ *   O_acc = e^(m - m_new) O_acc + e^(m~ - m_new) (P~ V)
+ * and O = O_acc / l only after the last key block (v2 defers the division).
+ * The query partition is q_cuts, the key partition kv_cuts (boundaries, both
+ * starting at 0 and ending at n_q / n_kv).  Rows of a query block are
+ * independent, so each row is carried through the key blocks on its own.
+ * o: [n_q, d], lse: [n_q].
+ */
+int fa_oracle_blockwise(const double *q, const double *k, const double *v,
+                        int64_t n_q, int64_t n_kv, int64_t d, double scale, int causal,
+                        const int64_t *q_cuts, int64_t n_qcuts,
+                        const int64_t *kv_cuts, int64_t n_kvcuts,
+                        double *o, double *lse)
+{
+    if (!q || !k || !v || !o || !lse || n_q < 1 || n_kv < 1 || d < 1) return 1;
+    if (!valid_cuts(q_cuts, n_qcuts, n_q) || !valid_cuts(kv_cuts, n_kvcuts, n_kv)) return 1;
+    int status = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)n_kv * sizeof(double));
+        double *pv = (double *)malloc((size_t)d * sizeof(double));
+        if (!s || !pv) {
+#pragma omp atomic write
+            status = 2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t qb = 0; qb < n_qcuts - 1; ++qb) {
+            if (!s || !pv) continue;
+            for (int64_t i = q_cuts[qb]; i < q_cuts[qb + 1]; ++i) {
+                const double *qi = q + i * d;
+                int64_t nv = visible_keys(i, n_kv, causal);
+                double m = -INFINITY, l = 0.0;
+                double *acc = o + i * d;
+                for (int64_t c = 0; c < d; ++c) acc[c] = 0.0;
+                for (int64_t kb = 0; kb < n_kvcuts - 1; ++kb) {
+                    int64_t a = kv_cuts[kb];
+                    int64_t b = kv_cuts[kb + 1] < nv ? kv_cuts[kb + 1] : nv;
+                    if (b <= a) continue; /* no visible key in this block */
+                    /* block scores and block max m~ */
+                    double mt = -INFINITY;
+                    for (int64_t j = a; j < b; ++j) {
+                        s[j] = score(qi, k + j * d, d, scale);
+                        if (s[j] > mt) mt = s[j];
+                    }
+                    /* P~ = exp(s - m~), l~ = sum P~, P~ V */
+                    double lt = 0.0;
+                    for (int64_t c = 0; c < d; ++c) pv[c] = 0.0;
+                    for (int64_t j = a; j < b; ++j) {
+                        double pj = exp(s[j] - mt);
+                        lt += pj;
+                        const double *vj = v + j * d;
+                        for (int64_t c = 0; c < d; ++c) pv[c] += pj * vj[c];
+                    }
+                    /* merge (plate 08) */
+                    double m_new = m > mt ? m : mt;
+                    double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+                    double beta = exp(mt - m_new);
+                    l = alpha * l + beta * lt;
+                    for (int64_t c = 0; c < d; ++c) acc[c] = alpha * acc[c] + beta * pv[c];
+                    m = m_new;
+                }
+                for (int64_t c = 0; c < d; ++c) acc[c] /= l;
+                lse[i] = m + log(l);
+            }
+        }
+        free(s);
+        free(pv);
+    }
+    return status;
+}
+
+/*
+ * Blockwise forward in v1 loop order ("Flash Attention 原理与实践" section
+ * 2.3): key blocks outside, query blocks inside; after every step the
+ * normalised output O, the sum l and the max m of each row are written back,
+ * and the step's update is
+ *   O_new = (l e^(m - m_new) O + e^(m~ - m_new) P~ V) / l_new.
+ * Block counts use the ceiling (the listing's floor would drop a ragged
+ * tail).  o: [n_q, d], lse: [n_q]; m_buf, l_buf: scratch [n_q] each.
+ */
+int fa_oracle_blockwise_v1(const double *q, const double *k, const double *v,
+                           int64_t n_q, int64_t n_kv, int64_t d, double scale, int causal,
+                           const int64_t *q_cuts, int64_t n_qcuts,
+                           const int64_t *kv_cuts, int64_t n_kvcuts,
+                           double *o, double *lse)
+{
+    if (!q || !k || !v || !o || !lse || n_q < 1 || n_kv < 1 || d < 1) return 1;
+    if (!valid_cuts(q_cuts, n_qcuts, n_q) || !valid_cuts(kv_cuts, n_kvcuts, n_kv)) return 1;
+    double *m_buf = (double *)malloc((size_t)n_q * sizeof(double));
+    double *l_buf = (double *)malloc((size_t)n_q * sizeof(double));
+    double *s = (double *)malloc((size_t)n_kv * sizeof(double));
+    double *pv = (double *)malloc((size_t)d * sizeof(double));
+    if (!m_buf || !l_buf || !s || !pv) {
+        free(m_buf); free(l_buf); free(s); free(pv);
+        return 2;
+    }
+    for (int64_t i = 0; i < n_q; ++i) {
+        m_buf[i] = -INFINITY;
+        l_buf[i] = 0.0;
+        for (int64_t c = 0; c < d; ++c) o[i * d + c] = 0.0;
+    }
+    for (int64_t kb = 0; kb < n_kvcuts - 1; ++kb) {
+        for (int64_t qb = 0; qb < n_qcuts - 1; ++qb) {
+            for (int64_t i = q_cuts[qb]; i < q_cuts[qb + 1]; ++i) {
+                const double *qi = q + i * d;
+                int64_t nv = visible_keys(i, n_kv, causal);
+                int64_t a = kv_cuts[kb];
+                int64_t b = kv_cuts[kb + 1] < nv ? kv_cuts[kb + 1] : nv;
+                if (b <= a) continue;
+                double mt = -INFINITY;
+                for (int64_t j = a; j < b; ++j) {
+                    s[j] = score(qi, k + j * d, d, scale);
+                    if (s[j] > mt) mt = s[j];
+                }
+                double lt = 0.0;
+                for (int64_t c = 0; c < d; ++c) pv[c] = 0.0;
+                for (int64_t j = a; j < b; ++j) {
+                    double pj = exp(s[j] - mt);
+                    lt += pj;
+                    for (int64_t c = 0; c < d; ++c) pv[c] += pj * v[j * d + c];
+                }
+                double mi = m_buf[i], li = l_buf[i];
+                double m_new = mi > mt ? mi : mt;
+                double old_w = (mi == -INFINITY) ? 0.0 : li * exp(mi - m_new);
+                double new_w = exp(mt - m_new);
+                double l_new = old_w + new_w * lt;
+                double *oi = o + i * d;
+                for (int64_t c = 0; c < d; ++c) oi[c] = (old_w * oi[c] + new_w * pv[c]) / l_new;
+                m_buf[i] = m_new;
+                l_buf[i] = l_new;
+            }
+        }
+    }
+    for (int64_t i = 0; i < n_q; ++i) lse[i] = m_buf[i] + log(l_buf[i]);
+    free(m_buf); free(l_buf); free(s); free(pv);
+    return 0;
+}
+
+/*
+ * OCP 8-bit floating point E4M3 ("fn" variant) to double: 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
+ * subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN and there are no
+ * infinities; largest finite magnitude 1.75 * 2^8 = 448.
+ */
+double fa_oracle_e4m3_to_double(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int mant = code & 0x7;
+    double mag;
+    if (e == 0xF && mant == 0x7) return NAN;
+    if (e == 0) mag = ldexp((double)mant, -9);
+    else mag = ldexp(1.0 + mant / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Decodes n E4M3 codes and multiplies each by descale (the product of two
+ * doubles with 4 and 24 significant bits is exact). */
+int fa_oracle_dequant_e4m3(const uint8_t *codes, int64_t n, double descale, double *out)
+{
+    if ((!codes || !out) && n > 0) return 1;
+    for (int64_t t = 0; t < n; ++t) out[t] = fa_oracle_e4m3_to_double(codes[t]) * descale;
+    return 0;
+}
