@@ -1,0 +1,206 @@
+// Host side of the C ABI declared in include/fa.h: argument validation
+// (pure host code, no HIP call), variant selection and kernel launch.
+#include <hip/hip_runtime_api.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace fa {
+const Variant *variants16(int *count);
+const Variant *variants32(int *count);
+const Variant *variants8(int *count);
+
+const Variant *variants(int *count) {
+    static std::vector<Variant> all = [] {
+        std::vector<Variant> v;
+        const Variant *(*parts[])(int *) = {variants32, variants16, variants8};
+        for (auto part : parts) {
+            int n = 0;
+            const Variant *t = part(&n);
+            v.insert(v.end(), t, t + n);
+        }
+        return v;
+    }();
+    *count = (int)all.size();
+    return all.data();
+}
+}  // namespace fa
+
+namespace {
+
+const fa::Variant *find_variant(int dtype, int64_t d, int causal, int which) {
+    int n = 0;
+    const fa::Variant *t = fa::variants(&n);
+    int seen = 0;
+    for (int i = 0; i < n; ++i) {
+        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0)) {
+            ++seen;
+            if (seen == (which <= 0 ? 1 : which)) return &t[i];
+        }
+    }
+    return nullptr;
+}
+
+int in_size(int dtype) { return dtype == FA_F32 ? 4 : dtype == FA_FP8_E4M3 ? 1 : 2; }
+int out_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+    if (na <= 0 || nb <= 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// float32 value of |scale| * log2(e) [* descale_q * descale_k], rounded once.
+double score_factor(const fa_fwd_args *a) {
+    double c = fabs((double)a->scale) * 1.4426950408889634;
+    if (a->dtype == FA_FP8_E4M3) c *= (double)a->descale_q * (double)a->descale_k;
+    return c;
+}
+
+const int64_t kMaxRows = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" int fa_validate(const fa_fwd_args *a) {
+    if (!a) return FA_ERR_NULL;
+    if (a->dtype < FA_F32 || a->dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
+    if (a->d != 64 && a->d != 128 && a->d != 256) return FA_ERR_HEAD_DIM;
+    if (a->B < 0 || a->H < 0 || a->N_q < 0 || a->N_kv < 1) return FA_ERR_SHAPE;
+    if (a->N_q > kMaxRows || a->N_kv > kMaxRows) return FA_ERR_SHAPE;
+    if (a->B > 0 && a->H > INT32_MAX / a->B) return FA_ERR_SHAPE;
+    const int64_t bh = a->B * a->H;
+    // every tensor byte count must fit int64 and the grid must fit 2^31 workgroups
+    if (bh > 0 && (a->N_q > INT64_MAX / 4 / a->d / bh || a->N_kv > INT64_MAX / 4 / a->d / bh))
+        return FA_ERR_SHAPE;
+    if (bh > 0 && (a->N_q + 31) / 32 > INT32_MAX / bh) return FA_ERR_SHAPE;
+    if (!isfinite(a->scale)) return FA_ERR_SCALE;
+    if (a->dtype == FA_FP8_E4M3 &&
+        (!isfinite(a->descale_q) || !isfinite(a->descale_k) || !isfinite(a->descale_v)))
+        return FA_ERR_SCALE;
+    if (!isfinite((float)score_factor(a))) return FA_ERR_SCALE;
+    if (fa_num_variants(a->dtype, a->d, a->causal) == 0) return FA_ERR_HEAD_DIM;
+    if (a->tile_override < 0 || a->tile_override > fa_num_variants(a->dtype, a->d, a->causal))
+        return FA_ERR_VARIANT;
+    if (bh == 0 || a->N_q == 0) return FA_OK;  // nothing to read or write
+    if (!a->Q || !a->K || !a->V || !a->O) return FA_ERR_NULL;
+    if (((uintptr_t)a->Q | (uintptr_t)a->K | (uintptr_t)a->V | (uintptr_t)a->O) & 15)
+        return FA_ERR_ALIGN;
+    if ((uintptr_t)a->LSE & 3) return FA_ERR_ALIGN;
+    const int64_t qb = bh * a->N_q * a->d * in_size(a->dtype);
+    const int64_t kb = bh * a->N_kv * a->d * in_size(a->dtype);
+    const int64_t ob = bh * a->N_q * a->d * out_size(a->dtype);
+    const int64_t lb = a->LSE ? bh * a->N_q * 4 : 0;
+    if (overlap(a->O, ob, a->Q, qb) || overlap(a->O, ob, a->K, kb) || overlap(a->O, ob, a->V, kb))
+        return FA_ERR_ALIAS;
+    if (lb && (overlap(a->LSE, lb, a->Q, qb) || overlap(a->LSE, lb, a->K, kb) ||
+               overlap(a->LSE, lb, a->V, kb) || overlap(a->LSE, lb, a->O, ob)))
+        return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
+extern "C" int fa_num_variants(int dtype, int64_t d, int causal) {
+    int n = 0, count = 0;
+    const fa::Variant *t = fa::variants(&n);
+    for (int i = 0; i < n; ++i)
+        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0)) ++count;
+    return count;
+}
+
+extern "C" const char *fa_variant_name(int dtype, int64_t d, int causal, int v) {
+    if (v < 1) return "";
+    const fa::Variant *x = find_variant(dtype, d, causal, v);
+    return x ? x->name : "";
+}
+
+extern "C" const char *fa_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "success";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "invalid shape (B, H, N_q < 0, N_kv < 1, or size overflow)";
+        case FA_ERR_HEAD_DIM: return "unsupported head dimension for this dtype";
+        case FA_ERR_DTYPE: return "unknown dtype";
+        case FA_ERR_ALIGN: return "misaligned pointer (Q, K, V, O need 16 bytes, LSE 4)";
+        case FA_ERR_SCALE: return "scale or descale not finite (also scale*log2(e)*descales in float32)";
+        case FA_ERR_ALIAS: return "output overlaps an input or the other output";
+        case FA_ERR_DEVICE: return "no usable gfx950 device";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_VARIANT: return "tile_override names no compiled variant";
+        default: return "unknown status";
+    }
+}
+
+namespace {
+
+// 1 if the current device is a gfx950, cached per device ordinal.
+int device_ok() {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, -1);
+    if (cache[dev] < 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+        cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    }
+    return cache[dev];
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_ex(const fa_fwd_args *a) {
+    const int st = fa_validate(a);
+    if (st != FA_OK) return st;
+    if (a->B * a->H == 0 || a->N_q == 0) return FA_OK;
+    if (!device_ok()) return FA_ERR_DEVICE;
+    const fa::Variant *v = find_variant(a->dtype, a->d, a->causal, a->tile_override);
+    if (!v) return FA_ERR_VARIANT;
+    fa::KParams p;
+    p.q = (const char *)a->Q;
+    p.k = (const char *)a->K;
+    p.v = (const char *)a->V;
+    p.o = (char *)a->O;
+    p.lse = a->LSE;
+    p.n_bh = (int)(a->B * a->H);
+    p.n_q = (int)a->N_q;
+    p.n_kv = (int)a->N_kv;
+    p.n_qblk = (int)((a->N_q + v->br - 1) / v->br);
+    p.n_wg = p.n_bh * p.n_qblk;
+    p.c = (float)score_factor(a);
+    p.o_mul = a->dtype == FA_FP8_E4M3 ? a->descale_v : 1.0f;
+    p.neg = a->scale < 0 ? 1 : 0;
+    (void)hipGetLastError();  // clear a stale error so it is not reported as ours
+    return v->launch(p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int64_t B,
+                      int64_t H, int64_t N_q, int64_t N_kv, int64_t d, float scale, int causal,
+                      int dtype) {
+    fa_fwd_args a;
+    memset(&a, 0, sizeof a);
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.LSE = LSE;
+    a.B = B;
+    a.H = H;
+    a.N_q = N_q;
+    a.N_kv = N_kv;
+    a.d = d;
+    a.scale = scale;
+    a.causal = causal;
+    a.dtype = dtype;
+    a.descale_q = a.descale_k = a.descale_v = 1.0f;
+    a.stream = nullptr;
+    a.tile_override = 0;
+    return fa_fwd_ex(&a);
+}

@@ -1,0 +1,73 @@
+// Device-side building blocks shared by the forward kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4v __attribute__((vector_size(8)));
+typedef int i32x2v __attribute__((vector_size(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Wave index as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// Asynchronous 16-byte copy global -> LDS.  Lane i of the wave writes to
+// lds_wave_base + 16 * i; lds_wave_base must be the same in every lane.
+__device__ __forceinline__ void copy16_to_lds(const void *gsrc, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (FA_LDS void *)lds_wave_base, 16, 0, 0);
+}
+
+// Waits until every outstanding global load of this wave (including the
+// direct-to-LDS copies) has completed.
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposed 64-bit LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the address of 4 consecutive 16-bit elements; lane i
+// receives element (i % 4) of the chunks addressed by lanes i/4, 4 + i/4,
+// 8 + i/4 and 12 + i/4, in that order.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *p) {
+    i16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4v *)p);
+    return __builtin_bit_cast(i16x4, r);
+}
+
+// Transposed 64-bit LDS read of 8-bit elements (ds_read_b64_tr_b8): within
+// each group of 16 lanes, lane j supplies the address of 8 consecutive bytes;
+// lane i receives byte (i % 8) of the chunks addressed by lanes
+// i/8, 2 + i/8, ..., 14 + i/8, in that order.
+__device__ __forceinline__ i32x2v lds_read_tr8(const void *p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2v *)p);
+}
+
+// Maps the hardware workgroup index to a logical one so that consecutive
+// logical indices (the query blocks of one head) land on the same XCD:
+// workgroups are dispatched to the 8 XCDs round-robin, and each XCD has its
+// own L2, so a head's K/V tiles are then fetched from HBM once per XCD.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    const int per = n >> 3;
+    if (bid < (per << 3)) return (bid & 7) * per + (bid >> 3);
+    return bid;
+}
+
+}  // namespace fa

@@ -1,0 +1,42 @@
+// Internal interface between the host dispatcher (fa_api.cpp) and the kernel
+// translation units (fa_fwd*.hip).  Not part of the C ABI.
+#pragma once
+#include <stdint.h>
+
+namespace fa {
+
+// Kernel arguments shared by every forward kernel.  Byte pointers; each
+// (batch, head) slice is contiguous, [n_q, d] for Q/O and [n_kv, d] for K/V.
+struct KParams {
+    const char *q;
+    const char *k;
+    const char *v;
+    char *o;
+    float *lse;        // may be null
+    int n_bh;          // B * H
+    int n_q;
+    int n_kv;
+    int n_qblk;        // ceil(n_q / BR)
+    int n_wg;          // n_bh * n_qblk
+    float c;           // |scale| * log2(e) (times descale_q * descale_k for E4M3)
+    float o_mul;       // factor applied to O at the end (descale_v for E4M3, else 1)
+    int neg;           // 1 if scale < 0: Q is negated on load and c = |scale|*log2(e)
+};
+
+// A compiled kernel instance and the query-block height it uses.
+typedef int (*launch_fn)(const KParams &p, void *stream);
+
+struct Variant {
+    int dtype;         // fa_dtype
+    int d;             // head dimension
+    int causal;        // 0 or 1
+    int br;            // query rows per workgroup
+    const char *name;
+    launch_fn launch;
+};
+
+// Every compiled variant, grouped by (dtype, d, causal); within a group the
+// first entry is the default.
+const Variant *variants(int *count);
+
+}  // namespace fa

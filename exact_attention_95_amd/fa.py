@@ -1,0 +1,170 @@
+"""ctypes binding of the C ABI in include/fa.h (argument marshalling only).
+
+The functions ``fa_fwd``, ``fa_fwd_ex``, ``fa_validate``, ``fa_strerror``,
+``fa_num_variants`` and ``fa_variant_name`` mirror the C entry points of the
+same names.  ``fwd`` is the torch convenience form: it allocates O and LSE
+with torch on the inputs' device and calls ``fa_fwd_ex`` on torch's current
+stream.  All attention arithmetic runs in the HIP kernels; there is no CPU
+path, and the library must have been built (``exact_attention_95_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
+(FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_SCALE,
+ FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT) = range(11)
+
+EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
+            "fa_variant_name")
+
+
+class FaFwdArgs(ctypes.Structure):
+    """Mirror of ``fa_fwd_args``."""
+
+    _fields_ = [
+        ("Q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
+        ("O", ctypes.c_void_p), ("LSE", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N_q", ctypes.c_int64),
+        ("N_kv", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
+        ("descale_v", ctypes.c_float),
+        ("stream", ctypes.c_void_p), ("tile_override", ctypes.c_int),
+    ]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__("fa status %d: %s" % (status, fa_strerror(status)))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Loads libfa.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("HIP library %s is not built; run exact_attention_95_amd.build"
+                                   % path)
+            lib = ctypes.CDLL(path)
+            i64, vp = ctypes.c_int64, ctypes.c_void_p
+            lib.fa_fwd.restype = ctypes.c_int
+            lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                   ctypes.c_int, ctypes.c_int]
+            lib.fa_fwd_ex.restype = ctypes.c_int
+            lib.fa_fwd_ex.argtypes = [ctypes.POINTER(FaFwdArgs)]
+            lib.fa_validate.restype = ctypes.c_int
+            lib.fa_validate.argtypes = [ctypes.POINTER(FaFwdArgs)]
+            lib.fa_strerror.restype = ctypes.c_char_p
+            lib.fa_strerror.argtypes = [ctypes.c_int]
+            lib.fa_num_variants.restype = ctypes.c_int
+            lib.fa_num_variants.argtypes = [ctypes.c_int, i64, ctypes.c_int]
+            lib.fa_variant_name.restype = ctypes.c_char_p
+            lib.fa_variant_name.argtypes = [ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
+            _lib = lib
+        return _lib
+
+
+def fa_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, causal, dtype) -> int:
+    """Raw ``fa_fwd``: pointers as ints (device addresses), returns the status."""
+    return load().fa_fwd(Q, K, V, O, LSE, B, H, N_q, N_kv, d, scale, int(causal), dtype)
+
+
+def fa_fwd_ex(args: FaFwdArgs) -> int:
+    return load().fa_fwd_ex(ctypes.byref(args))
+
+
+def fa_validate(args: FaFwdArgs) -> int:
+    return load().fa_validate(ctypes.byref(args))
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(status).decode()
+
+
+def fa_num_variants(dtype: int, d: int, causal: bool) -> int:
+    return load().fa_num_variants(dtype, d, int(bool(causal)))
+
+
+def fa_variant_name(dtype: int, d: int, causal: bool, v: int) -> str:
+    return load().fa_variant_name(dtype, d, int(bool(causal)), v).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16,
+             torch.float8_e4m3fn: FA_FP8_E4M3}
+    if t.dtype not in codes:
+        raise TypeError("unsupported dtype %s" % t.dtype)
+    return codes[t.dtype]
+
+
+def make_args(q, k, v, o, lse, scale: float, causal: bool, descale=(1.0, 1.0, 1.0),
+              stream=None, tile: int = 0) -> FaFwdArgs:
+    """fa_fwd_args for torch tensors q [B,H,N_q,d], k/v [B,H,N_kv,d], o, lse."""
+    B, H, N_q, d = q.shape
+    a = FaFwdArgs()
+    a.Q, a.K, a.V, a.O = q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr()
+    a.LSE = lse.data_ptr() if lse is not None else None
+    a.B, a.H, a.N_q, a.N_kv, a.d = B, H, N_q, k.shape[2], d
+    a.scale = scale
+    a.causal = int(bool(causal))
+    a.dtype = _dtype_code(q)
+    a.descale_q, a.descale_k, a.descale_v = (float(x) for x in descale)
+    a.stream = stream
+    a.tile_override = tile
+    return a
+
+
+def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None, out=None,
+        lse=None, with_lse: bool = True, stream=None, tile: int = 0):
+    """Attention forward of torch device tensors; returns (O, LSE).
+
+    q: [B,H,N_q,d]; k, v: [B,H,N_kv,d]; all contiguous, same dtype, on one
+    gfx950 device.  scale defaults to 1/sqrt(d) (as float32).  For
+    float8_e4m3fn inputs, descale = (descale_q, descale_k, descale_v) and O is
+    bfloat16.  ``stream``: a torch stream or raw hipStream_t (default: torch's
+    current stream).
+    """
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise RuntimeError("fa.fwd needs GPU tensors; there is no CPU path")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected [B,H,N,d] tensors")
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                              tuple(v.shape)))
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    B, H, N_q, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is None:
+        out = torch.empty((B, H, N_q, d), dtype=out_dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args = make_args(q, k, v, out, lse, scale, causal, descale or (1.0, 1.0, 1.0), stream, tile)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_ex(args)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse

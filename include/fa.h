@@ -1,0 +1,136 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The operation is the attention of "FlashAttention算子优化" section 2 and
+ * of "FlashAttention 与显存" plates 04, 07 and 08: for every batch b and head
+ * h,
+ *     S = scale * Q K^T            ([N_q, N_kv] scores; never stored)
+ *     P = softmax(S) row by row    (with the causal mask, if requested)
+ *     O = P V                      ([N_q, d])
+ *     LSE_i = ln(sum_j exp(S_ij))  (the per-row statistic that plate 09 keeps
+ *                                   for the backward pass, in one number)
+ * computed tile by tile with the online softmax, so S and P never reach HBM.
+ * The result equals the definition up to floating-point rounding.
+ *
+ * Layout.  Q is [B, H, N_q, d]; K and V are [B, H, N_kv, d]; O is
+ * [B, H, N_q, d]; LSE is [B, H, N_q].  All are dense row-major with d the
+ * fastest dimension (the per-(batch, head) [N, d] slices of the section-2
+ * pseudocode of "FlashAttention算子优化", stacked).
+ *
+ * Element types.  FA_F32, FA_F16 and FA_BF16 inputs produce O of the same
+ * type.  FA_FP8_E4M3 inputs (OCP E4M3, per-tensor descales, see
+ * fa_fwd_args) produce O in bfloat16.  LSE is always float32, natural log,
+ * of the scaled (and masked) scores.
+ *
+ * Causal mask.  When causal != 0, key j is visible to query i iff j <= i
+ * (top-left alignment, also when N_q != N_kv); no row is ever fully masked.
+ *
+ * Memory.  Q, K, V, O and LSE are device pointers on the current HIP device,
+ * owned by the caller.  Q, K, V are read-only; O and LSE are written in
+ * full.  The library allocates nothing and keeps no mutable global state, so
+ * calls on different streams may run concurrently.  Calls are asynchronous
+ * with respect to the host; errors raised while a kernel runs surface at the
+ * caller's next synchronisation.
+ *
+ * Errors.  Every entry point returns 0 (FA_OK) or an fa_status code;
+ * fa_strerror() names it.  Arguments are validated on the host, before any
+ * HIP call; no C++ exception crosses this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_F32 = 0,
+    FA_F16 = 1,
+    FA_BF16 = 2,
+    FA_FP8_E4M3 = 3
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer (Q, K, V, O, args) is NULL */
+    FA_ERR_SHAPE = 2,     /* B, H or N_q < 0, N_kv < 1, or a size overflows */
+    FA_ERR_HEAD_DIM = 3,  /* d not in {64, 128, 256} */
+    FA_ERR_DTYPE = 4,     /* dtype not an fa_dtype value */
+    FA_ERR_ALIGN = 5,     /* Q, K, V or O not 16-byte aligned, LSE not 4-byte aligned */
+    FA_ERR_SCALE = 6,     /* scale or a descale is not finite */
+    FA_ERR_ALIAS = 7,     /* O or LSE overlaps Q, K, V, or each other */
+    FA_ERR_DEVICE = 8,    /* no usable gfx950 device / HIP runtime error before launch */
+    FA_ERR_LAUNCH = 9,    /* the kernel launch failed */
+    FA_ERR_VARIANT = 10   /* tile_override names no compiled variant for this problem */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward on the null stream.
+ *
+ * Q, K, V: device inputs (see Layout); O: device output; LSE: device
+ * float32 output, or NULL to skip it.  B, H >= 0 batches and heads;
+ * N_q >= 0 query rows and N_kv >= 1 key rows per head; d in {64, 128, 256}.
+ * B, H or N_q equal to 0 is a successful no-op.  scale multiplies QK^T
+ * before the softmax (1/sqrt(d) in the pages); any finite value is valid,
+ * including 0 and negative values.  causal: 0 or non-zero (see Causal
+ * mask).  dtype: an fa_dtype; FA_FP8_E4M3 needs fa_fwd_ex for descales
+ * other than 1.
+ */
+int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+           int64_t B, int64_t H, int64_t N_q, int64_t N_kv, int64_t d,
+           float scale, int causal, int dtype);
+
+/*
+ * Full argument set.  descale_q/k/v multiply the decoded E4M3 values of Q,
+ * K and V (only read for FA_FP8_E4M3; must be finite).  stream is a
+ * hipStream_t (NULL = null stream).  tile_override selects a compiled tile
+ * variant (0 = the library's choice; 1..fa_num_variants() for tuning and
+ * cross-checks).
+ */
+typedef struct {
+    const void *Q;
+    const void *K;
+    const void *V;
+    void *O;
+    float *LSE;
+    int64_t B, H, N_q, N_kv, d;
+    float scale;
+    int causal;
+    int dtype;
+    float descale_q, descale_k, descale_v;
+    void *stream;
+    int tile_override;
+} fa_fwd_args;
+
+/* Attention forward with the full argument set (see fa_fwd_args). */
+int fa_fwd_ex(const fa_fwd_args *args);
+
+/*
+ * Validates args exactly as fa_fwd_ex does, without any HIP call (usable
+ * on a machine without a GPU).  Returns FA_OK or the status fa_fwd_ex would
+ * return before launching.
+ */
+int fa_validate(const fa_fwd_args *args);
+
+/* Static, never-NULL description of a status code. */
+const char *fa_strerror(int status);
+
+/*
+ * Number of compiled tile variants for (dtype, d, causal), 0 if the
+ * combination is unsupported.  Host-only, no HIP call.
+ */
+int fa_num_variants(int dtype, int64_t d, int causal);
+
+/*
+ * Static description of variant v (1-based) for (dtype, d, causal), e.g.
+ * "br256_bc64_w8"; "" if v is out of range.  Host-only, no HIP call.
+ */
+const char *fa_variant_name(int dtype, int64_t d, int causal, int v);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,98 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the oracle on
+the same seeded inputs and measure the disagreement."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from exact_attention_95_amd import fa
+from exact_attention_95_amd.inputs import Workload, make_inputs
+
+# Tolerances on O (max abs, relative L2 over the whole tensor) and on LSE (max abs).
+TOL = {"f32": (1e-5, 1e-6), "f16": (2e-2, 5e-3), "bf16": (2e-2, 5e-3), "fp8_e4m3": (None, 5e-2)}
+LSE_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_operands(w: Workload, x: dict):
+    """Exact values the kernel sees, as the oracle's inputs (E4M3: code * descale)."""
+    if w.dtype == "fp8_e4m3":
+        dq, dk, dv = x["descale"]
+        return (oracle.dequant_e4m3(x["q"], dq), oracle.dequant_e4m3(x["k"], dk),
+                oracle.dequant_e4m3(x["v"], dv))
+    return x["q"], x["k"], x["v"]
+
+
+def run_gpu(w: Workload, x: dict, tile: int = 0, device="cuda:0"):
+    q, k, v = (x[n].to(device) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, scale=w.sm_scale, causal=w.causal, descale=x["descale"], tile=tile)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def errors(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray) -> dict:
+    diff = o_gpu - o_ref
+    return {
+        "max_abs": float(np.abs(diff).max()) if diff.size else 0.0,
+        "rel_l2": float(np.linalg.norm(diff) / max(np.linalg.norm(o_ref), 1e-300)) if diff.size else 0.0,
+        "lse_max_abs": float(np.abs(lse_gpu - lse_ref).max()) if lse_ref.size else 0.0,
+        "finite": bool(np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all()),
+    }
+
+
+def assert_within(w: Workload, err: dict, label: str = ""):
+    max_abs, rel = TOL[w.dtype]
+    msg = "%s %s %s" % (w.name, label, err)
+    assert err["finite"], msg
+    if max_abs is not None:
+        assert err["max_abs"] <= max_abs, msg
+    assert err["rel_l2"] <= rel, msg
+    assert err["lse_max_abs"] <= LSE_TOL, msg
+
+
+def full_parity(w: Workload, tile: int = 0, x: dict | None = None) -> dict:
+    """Whole-tensor comparison (sizes the oracle finishes in seconds)."""
+    x = x or make_inputs(w)
+    o, lse = run_gpu(w, x, tile)
+    qo, ko, vo = oracle_operands(w, x)
+    o_ref, lse_ref = oracle.attention(qo, ko, vo, w.sm_scale, w.causal)
+    return errors(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref)
+
+
+def sample_rows(w: Workload, x: dict, br: int, n_random: int = 512, heads: int = 4,
+                seed: int = 0) -> np.ndarray:
+    """Rows to check at full size: every boosted row, random rows, both rows
+    around every query-block boundary and the first/last rows of a few heads."""
+    rng = np.random.default_rng([w.seed_id, 99, seed])
+    n = w.n_q
+    picks = [x["boost_rows"]]
+    bh_all = w.B * w.H
+    hs = rng.choice(bh_all, size=min(heads, bh_all), replace=False)
+    for bh in hs:
+        base = bh * n
+        picks.append(base + rng.integers(0, n, n_random // len(hs)))
+        edges = np.arange(br, n, br)
+        picks.append(base + np.concatenate([[0, n - 1], edges - 1, edges])[:256])
+    rows = np.unique(np.concatenate(picks).astype(np.int64))
+    return rows
+
+
+def sampled_parity(w: Workload, br: int, tile: int = 0, **kw) -> dict:
+    x = make_inputs(w)
+    o, lse = run_gpu(w, x, tile)
+    rows = sample_rows(w, x, br, **kw)
+    o_s = o.reshape(-1, w.d)[torch.from_numpy(rows).to(o.device)].double().cpu().numpy()
+    l_s = lse.reshape(-1)[torch.from_numpy(rows).to(o.device)].double().cpu().numpy()
+    del o, lse
+    qo, ko, vo = oracle_operands(w, x)
+    o_ref, lse_ref = oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
+    err = errors(o_s, l_s, o_ref, lse_ref)
+    err["rows"] = int(rows.size)
+    return err
