@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Attention-forward throughput on one MI355X.
+
+One step = one fa_fwd_ex call over the whole batch of the workload (every
+stage of the forward pass runs inside that launch).  Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
+
+Prints ONE JSON line with the throughput (attention TFLOP/s, FLOPs =
+4*B*H*N_q*N_kv*d, halved for causal), the dominant kernel's roofline
+position (algorithmic FLOPs per launch / average launch time from HIP
+events on the launch stream, against the bf16/fp16/fp8/fp32 dense MFMA
+peak) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attention fwd TFLOP/s (4·B·H·N²·d) and % of MFMA peak, "
+          "bf16 N=8K d=128")
+DEFAULT_WORKLOAD = "headline_bf16_n8192_d128"
+# MI355X dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x flop/clk/CU of the matrix cores
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8_e4m3": 5033.2, "f32": 157.3}
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    """Hash of the kernel sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_95_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, target_s: float = 12.0) -> dict:
+    """The fp64 oracle on a bounded row sample of the same workload."""
+    import oracle
+    from exact_attention_95_amd.inputs import boost_rows  # noqa: F401  (same generator)
+    rng = np.random.default_rng([w.seed_id, 7])
+    heads = rng.choice(w.B * w.H, size=min(4, w.B * w.H), replace=False)
+    per_row = 4.0 * w.n_kv * w.d  # non-causal rows; causal rows are sampled uniformly below
+
+    def sample(n_rows):
+        per_head = max(1, n_rows // len(heads))
+        rows = np.concatenate([bh * w.n_q + rng.integers(0, w.n_q, per_head) for bh in heads])
+        return rows.astype(np.int64)
+
+    def flops_of(rows):
+        i = rows % w.n_q
+        if w.causal:
+            return float(np.sum(4.0 * np.minimum(i + 1, w.n_kv) * w.d))
+        return per_row * rows.size
+
+    qo, ko, vo = x["q"], x["k"], x["v"]
+    if w.dtype == "fp8_e4m3":
+        dq, dk, dv = x["descale"]
+        qo, ko, vo = (oracle.dequant_e4m3(t, s) for t, s in ((qo, dq), (ko, dk), (vo, dv)))
+    # calibrate on a small sample, then size the measured one to ~target_s
+    rows = sample(64)
+    t0 = time.perf_counter()
+    oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    n = int(min(max(64, 64 * target_s / max(dt, 1e-3)), 200000))
+    rows = sample(n)
+    t0 = time.perf_counter()
+    oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
+    dt = time.perf_counter() - t0
+    f = flops_of(rows)
+    return {
+        "value": f / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d query rows (uniform over %d heads) of workload %s, fp64 three-pass "
+                  "oracle, %.1f s, %.3g FLOP" % (rows.size, len(heads), w.name, dt, f),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--tile", type=int, default=0, help="fa_fwd_args.tile_override")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the multi-GPU split (heads across GPUs, "
+              "no exchange) is not built.", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_attention_95_amd import fa
+    from exact_attention_95_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    out_dtype = torch.bfloat16 if w.dtype == "fp8_e4m3" else q.dtype
+    o = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream(device=dev)  # default priority
+    fargs = fa.make_args(q, k, v, o, lse, w.sm_scale, w.causal, x["descale"],
+                         stream.cuda_stream, args.tile)
+    st = fa.fa_validate(fargs)
+    if st != fa.FA_OK:
+        raise fa.FaError(st)
+
+    def step():
+        s = fa.fa_fwd_ex(fargs)
+        if s != fa.FA_OK:
+            raise fa.FaError(s)
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    if not bool(torch.isfinite(o.float()).all()):
+        print("non-finite output", file=sys.stderr)
+        return 1
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    flops = w.flops
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.n_q, "N_kv": w.n_kv,
+                   "d": w.d, "causal": w.causal, "dtype": w.dtype,
+                   "variant": fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1),
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": stored_traffic(w.name), "kernel_ms": round(kernel_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -80,6 +80,8 @@ def _declare(lib):
             _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64, _i64p,
             ctypes.c_int64, _dp, _dp]
+    lib.fa_oracle_num_threads.restype = ctypes.c_int
+    lib.fa_oracle_num_threads.argtypes = []
     lib.fa_oracle_e4m3_to_double.restype = ctypes.c_double
     lib.fa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.fa_oracle_dequant_e4m3.restype = ctypes.c_int
@@ -170,6 +172,11 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
         if return_p:
             p[sel] = ph
     return (o, lse, p) if return_p else (o, lse)
+
+
+def num_threads(lib=None) -> int:
+    """Threads the oracle's parallel loops use (OpenMP)."""
+    return int((lib or load()).fa_oracle_num_threads())
 
 
 def cuts_from_block(n: int, block: int) -> np.ndarray:

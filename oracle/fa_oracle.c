@@ -40,6 +40,19 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of threads a parallel region of this library uses. */
+int fa_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Number of keys row i may attend to. */
 static int64_t visible_keys(int64_t i, int64_t n_kv, int causal)
