@@ -2,6 +2,7 @@
 // (pure host code, no HIP call), variant selection and kernel launch.
 #include <hip/hip_runtime_api.h>
 
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -174,7 +175,10 @@ extern "C" int fa_fwd_ex(const fa_fwd_args *a) {
     p.n_kv = (int)a->N_kv;
     p.n_qblk = (int)((a->N_q + v->br - 1) / v->br);
     p.n_wg = p.n_bh * p.n_qblk;
-    p.c = (float)score_factor(a);
+    // c >= FLT_MIN keeps c > 0, so a masked score (-inf) always gives P = 0; for
+    // |scale * log2 e| below FLT_MIN every exp2 argument rounds to the same
+    // value as with the exact c (|s c| < 2^-25 gives exp2 = 1).
+    p.c = fmaxf((float)score_factor(a), FLT_MIN);
     p.o_mul = a->dtype == FA_FP8_E4M3 ? a->descale_v : 1.0f;
     p.neg = a->scale < 0 ? 1 : 0;
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours

@@ -20,10 +20,20 @@
 //   O^T += V_tile^T P^T          V^T operand read with ds_read_b64_tr_b16
 //
 // and after the last tile O = O_acc / l, LSE = (m + log2 l) ln 2 (v2 defers
-// the division to the end).  K/V tiles are double-buffered in LDS and filled
-// with direct global->LDS copies (global_load_lds_dwordx4) one tile ahead.
-// The causal variant stops at the diagonal tile (plate 07: the mask is fused
-// into the kernel) and masks only the tiles that straddle it.
+// the division to the end).
+//
+// The loop is software-pipelined by one tile: iteration j issues the MFMAs
+// of S_{j+1} = K_{j+1} Q^T, then the MFMAs of O += V_j^T P_j^T together with
+// the softmax (VALU) of S_{j+1}, so the exponentials of one tile overlap the
+// matrix products of the previous one.  A rescale of O decided by the
+// softmax of tile j+1 is applied at the start of iteration j+1, before P_{j+1}
+// is accumulated.  K and V tiles have two LDS buffers each and are filled by
+// direct global->LDS copies (global_load_lds_dwordx4): K two tiles ahead, V
+// one tile ahead.  The causal variant stops at the diagonal tile (plate 07:
+// the mask is fused into the kernel) and masks only the tiles that straddle
+// it.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "../../include/fa.h"
 
@@ -57,12 +67,13 @@ struct Cfg {
     static constexpr int KX = (NC < 16 ? NC : 16) - 1;    // K chunk swizzle mask
     static constexpr int VX = (NC / 4 < 4 ? NC / 4 : 4) - 1;  // V swizzle mask (4-chunk units)
     static constexpr int TILE = BC * RB;                  // bytes of one K or V tile
-    static constexpr int STAGE = 2 * TILE;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int LDS = 4 * TILE;                  // K0, K1, V0, V1
     static constexpr int KS = D / 16;                     // k-steps of S^T = K Q^T
     static constexpr int KB = BC / 32;                    // 32-key blocks per tile
     static constexpr int DB = D / 32;                     // 32-row blocks of O^T
-    static constexpr int LDI = TILE / (1024 * NW);        // copy instructions per wave per tensor
+    static constexpr int LDI = TILE / (1024 * NW);        // copy instructions per wave per tile
+    static constexpr int NKO = KS < 8 ? KS : 8;           // distinct K read offsets per lane
+    static constexpr int NVO = DB < 4 ? DB : 4;           // distinct V read offsets per lane
     static constexpr float TAU = 8.0f;
     static_assert(TILE % (1024 * NW) == 0, "tile must split into whole wave copies");
     static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
@@ -78,23 +89,177 @@ template <class C> __device__ __forceinline__ int kswz(int r) { return (r / C::R
 // spreads over 16 different bank groups.
 template <class C> __device__ __forceinline__ int vswz(int r) { return 4 * ((r / C::RPB) & C::VX); }
 
-// Issues the direct-to-LDS copies of key/value rows [t0, t0 + BC) of one
-// head into one LDS stage.  Rows past n_kv are clamped to the last row (their
-// scores are masked, their P entries are zero).
-template <class C>
-__device__ __forceinline__ void load_tile(const char *kh, const char *vh, int t0, int n_kv,
-                                          char *stage, int w, int lane) {
+// Issues the direct-to-LDS copies of rows [t0, t0 + BC) of one head's K (or
+// V, with vswz) into one LDS buffer.  Rows past n_kv are clamped to the last
+// row (their scores are masked and their P entries are zero).
+template <class C, bool IS_V>
+__device__ __forceinline__ void load_tile(const char *src, int t0, int n_kv, char *buf, int w,
+                                          int lane) {
 #pragma unroll
     for (int i = 0; i < C::LDI; ++i) {
-        const int cb = (i * C::NW + w) * 64;       // first chunk of this wave's copy
+        const int cb = (i * C::NW + w) * 64;  // first chunk of this wave's copy
         const int chunk = cb + lane;
         const int r = chunk / C::NC;
-        const int pc = chunk % C::NC;               // physical chunk in the LDS row
+        const int pc = chunk % C::NC;          // physical chunk in the LDS row
         int gr = t0 + r;
         gr = gr < n_kv ? gr : n_kv - 1;
-        const int64_t rowoff = (int64_t)gr * C::RB;
-        copy16_to_lds(kh + rowoff + 16 * (pc ^ kswz<C>(r)), stage + cb * 16);
-        copy16_to_lds(vh + rowoff + 16 * (pc ^ vswz<C>(r)), stage + C::TILE + cb * 16);
+        const int sw = IS_V ? vswz<C>(r) : kswz<C>(r);
+        copy16_to_lds(src + (int64_t)gr * C::RB + 16 * (pc ^ sw), buf + cb * 16);
+    }
+}
+
+// v_permlane32_swap(a, b) returns ([a_lo, b_lo], [a_hi, b_hi]) (lo = lanes
+// 0-31, hi = lanes 32-63).  With a = b = x every lane thus receives the lower
+// half's x in the first result and the upper half's x in the second.  The
+// second operand is an opaque copy of x: the compiler would otherwise treat
+// the two results of a swap of identical operands as interchangeable.
+__device__ __forceinline__ void both_halves(float x, float &lo, float &hi) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    unsigned v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "v"(u));
+    const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Maximum / sum over the two half-waves (lanes l and l ^ 32), in every lane.
+__device__ __forceinline__ float max_halves(float x) {
+    float lo, hi;
+    both_halves(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+    float lo, hi;
+    both_halves(x, lo, hi);
+    return lo + hi;
+}
+
+// S^T (32 keys x 32 queries per block) = K_tile Q^T.
+template <class C>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const char *Ks, const int (&koff)[C::NKO],
+                                        const typename Mma16<typename C::T>::v8 (&qf)[C::KS]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+        s[kb] = (f32x16){};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const v8 a = *(const v8 *)(Ks + kb * 32 * C::RB + koff[ks & 7] + 256 * (ks >> 3));
+            s[kb] = M::mma(a, qf[ks], s[kb]);
+        }
+    }
+}
+
+// O^T += V_tile^T P^T.  Register r of S^T block kb holds key
+// 32 kb + 8 (r/4) + 4 h + r%4, so the B operand of k-step (kb, k2) carries
+// keys 32 kb + 16 k2 + {0..3, 8..11} (+4 in the upper half-wave), and the
+// matching V^T operand is two transposed reads of 4 consecutive rows each.
+template <class C>
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[C::DB], const char *Vs, const int (&voff)[C::NVO],
+                                        const typename Mma16<typename C::T>::v8 (&pb)[C::KB][2]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + voff[db & 3] + 256 * (db >> 2);
+                const i16x4 lo = lds_read_tr16(base);
+                const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+                const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[db] = M::mma(a, pb[kb][k2], o[db]);
+            }
+}
+
+// Masks the scores of one S^T tile for this lane's query row qi: keys past
+// n_kv, and (causal) keys after qi, become -inf.
+template <class C>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[C::KB], int t0, int qi, int n_kv, int h) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool vis = key < n_kv && (!C::CAUSAL || key <= qi);
+            s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+}
+
+// Online-softmax step for one tile of S^T (this lane's query row): takes
+// the row max, raises the reference max m_use if the tile max exceeds it by
+// more than TAU (wave-uniform decision, returned in `raised` with the factor
+// alpha that O must still be multiplied by), and writes P = exp2(S c - m_use)
+// as the MFMA operand type into pb while accumulating this half-wave's share
+// of the row sum (of the float32 P, before rounding) into l_acc.  c > 0, so masked scores
+// (-inf) give P = 0.
+template <class C>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
+                                             typename Mma16<typename C::T>::v8 (&pb)[C::KB][2],
+                                             float &m_use, float &l_acc, float &alpha, bool &raised,
+                                             float c) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+    typedef typename C::T T;
+    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+    const float mt = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]))) * c;
+    raised = __any(mt > m_use + C::TAU);
+    const float m_new = raised ? fmaxf(m_use, mt) : m_use;
+    alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
+    l_acc *= alpha;
+    m_use = m_new;
+    const float mref = (m_use == kNegInf) ? 0.f : m_use;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mref));
+            l4[r & 3] += s[kb][r];
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            v8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (T)s[kb][8 * k2 + e];
+            pb[kb][k2] = x;
+        }
+    }
+    l_acc += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+}
+
+// Instruction order for the compiler's scheduler.  S^T MFMAs: each K read
+// one MFMA ahead.  PV MFMAs: each preceded by the two transposed V reads it
+// needs and followed by a share of the softmax VALU work, so that the
+// exponentials issue while the matrix core is busy and only a few operands
+// are in flight at a time.
+template <class C>
+__device__ __forceinline__ void schedule_qk() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < C::KB * C::KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+}
+template <class C>
+__device__ __forceinline__ void schedule_pv_softmax() {
+    constexpr int NPV = C::DB * C::KB * 2;
+    constexpr int VALU = 120 * C::KB / 2;  // softmax VALU instructions, about
+    constexpr int VPM = (VALU + NPV - 1) / NPV;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
     }
 }
 
@@ -105,6 +270,9 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     typedef typename M::v8 v8;
     typedef typename M::v4 v4;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    // LDS: K buffers 0 and 1, then V buffers 0 and 1
+    auto kbuf = [&](int i) { return smem + i * C::TILE; };
+    auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -125,17 +293,19 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     const char *kh = p.k + (int64_t)bh * n_kv * C::RB;
     const char *vh = p.v + (int64_t)bh * n_kv * C::RB;
 
-    const int ntile_all = (n_kv + C::BC - 1) / C::BC;
-    int ntile = ntile_all;
-    if (C::CAUSAL) {
-        const int qlast = min(q0 + C::BR - 1, n_q - 1);
-        ntile = min(ntile_all, qlast / C::BC + 1);
-    }
-    const int wq_last = min(wq0 + 31, n_q - 1);
-    const bool wave_has_rows = wq0 < n_q;
+    // tiles streamed by the workgroup, and tiles this wave computes
+    int ntile = (n_kv + C::BC - 1) / C::BC;
+    if (C::CAUSAL) ntile = min(ntile, min(q0 + C::BR - 1, n_q - 1) / C::BC + 1);
+    int wn = 0;
+    if (wq0 < n_q) wn = C::CAUSAL ? min(ntile, min(wq0 + 31, n_q - 1) / C::BC + 1) : ntile;
+    // tile t needs masking past n_kv, or when it reaches above this wave's first row
+    auto need_mask = [&](int t) {
+        return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
+    };
 
-    // Start streaming tile 0 while Q is loaded.
-    load_tile<C>(kh, vh, 0, n_kv, smem, w, lane);
+    load_tile<C, false>(kh, 0, n_kv, kbuf(0), w, lane);
+    load_tile<C, true>(vh, 0, n_kv, vbuf(0), w, lane);
+    if (ntile > 1) load_tile<C, false>(kh, C::BC, n_kv, kbuf(1), w, lane);
 
     // ---- Q^T operand: lane holds Q[qi][ks*16 + 8h .. +7] for every k-step ----
     v8 qf[C::KS];
@@ -152,23 +322,22 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
 
     // ---- per-lane LDS offsets (tile-independent parts) ----
     // K operand of k-step ks: row l32 of the 32-key block, logical chunk 2ks+h.
-    int koff[C::KS < 8 ? C::KS : 8];
+    int koff[C::NKO];
     {
         const int sw = kswz<C>(l32);
 #pragma unroll
-        for (int ks = 0; ks < (C::KS < 8 ? C::KS : 8); ++ks)
-            koff[ks] = l32 * C::RB + 16 * ((2 * ks + h) ^ sw);
+        for (int ks = 0; ks < C::NKO; ++ks) koff[ks] = l32 * C::RB + 16 * ((2 * ks + h) ^ sw);
     }
     // V^T operand via transposed reads: the 16-lane group g = lane/16 covers
-    // rows kbase + (lane%16)/4 and columns 32*dblk + 16*(g%2) + 4*(lane%4).
-    int voff[C::DB < 4 ? C::DB : 4];
+    // rows kbase + 4h + (lane%16)/4 and columns 32*dblk + 16*(g%2) + 4*(lane%4).
+    int voff[C::NVO];
     {
         const int j = lane & 15;
         const int rsub = 4 * h + (j >> 2);               // row within a group of 8
         const int x = vswz<C>(j >> 2) >> 2;              // swizzle of that row, in 4-chunk units
         const int y = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
 #pragma unroll
-        for (int db = 0; db < (C::DB < 4 ? C::DB : 4); ++db)
+        for (int db = 0; db < C::NVO; ++db)
             voff[db] = rsub * C::RB + 16 * (4 * (db ^ x) + y) + 8 * (j & 1);
     }
 
@@ -177,105 +346,55 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
     float m_use = kNegInf;   // reference max (log2 units) of this lane's query row
     float l_acc = 0.f;       // this half-wave's share of the row sum
+    float alpha = 1.f;       // pending rescale of O
+    bool raised = false;
     const float c = p.c;
+    v8 p0[C::KB][2], p1[C::KB][2];  // P of even / odd tiles
 
-    for (int t = 0; t < ntile; ++t) {
+    wait_vm();
+    __syncthreads();
+    if (wn > 0) {
+        f32x16 s[C::KB];
+        qk_tile<C>(s, kbuf(0), koff, qf);
+        if (need_mask(0)) mask_tile<C>(s, 0, qi, n_kv, h);
+        softmax_tile<C>(s, p0, m_use, l_acc, alpha, raised, c);
+        raised = false;  // O is still zero
+    }
+
+    // One pipelined iteration for tile t (t % 2 == PAR): S_{t+1} and the
+    // softmax of tile t+1 (into pn), PV of tile t (from pc).
+    auto iteration = [&](auto par, int t, v8 (&pc)[C::KB][2], v8 (&pn)[C::KB][2]) {
+        constexpr int PAR = decltype(par)::value;
         wait_vm();
         __syncthreads();
-        char *stage = smem + (t & 1) * C::STAGE;
-        if (t + 1 < ntile)
-            load_tile<C>(kh, vh, (t + 1) * C::BC, n_kv, smem + ((t + 1) & 1) * C::STAGE, w, lane);
-        const int t0 = t * C::BC;
-        if (!wave_has_rows || (C::CAUSAL && t0 > wq_last)) continue;
-
-        const char *Ks = stage;
-        const char *Vs = stage + C::TILE;
-
-        // ---- S^T = K Q^T ----
-        f32x16 s[C::KB];
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            s[kb] = (f32x16){};
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                const v8 a = *(const v8 *)(Ks + kb * 32 * C::RB + koff[ks & 7] + 256 * (ks >> 3));
-                s[kb] = M::mma(a, qf[ks], s[kb]);
-            }
-        }
-
-        // ---- mask (only tiles past n_kv or straddling the diagonal) ----
-        const bool need_mask = (t0 + C::BC > n_kv) || (C::CAUSAL && t0 + C::BC - 1 > wq0);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = key < n_kv && (!C::CAUSAL || key <= qi);
-                    s[kb][r] = vis ? s[kb][r] : kNegInf;
-                }
-        }
-
-        // ---- row max over the tile (in-lane, then across half-waves) ----
-        float mx = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt = (mx == kNegInf) ? kNegInf : mx * c;
-
-        // ---- online-softmax merge: raise the reference only when needed ----
-        if (__any(mt > m_use + C::TAU)) {
-            const float m_new = fmaxf(m_use, mt);
-            const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
-            l_acc *= alpha;
+        if (t + 2 < ntile) load_tile<C, false>(kh, (t + 2) * C::BC, n_kv, kbuf(PAR), w, lane);
+        if (t + 1 < ntile) load_tile<C, true>(vh, (t + 1) * C::BC, n_kv, vbuf(1 - PAR), w, lane);
+        if (t >= wn) return;
+        if (raised) {
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
-            m_use = m_new;
         }
-        const float mref = (m_use == kNegInf) ? 0.f : m_use;
-
-        // ---- P = exp2(S c - m), row sum, convert to the MFMA type ----
-        v8 pb[C::KB][2];
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mref));
-                if (need_mask) e = (s[kb][r] == kNegInf) ? 0.f : e;
-                s[kb][r] = e;
-                l_acc += e;
-            }
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                v8 x;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (T)s[kb][8 * k2 + e];
-                pb[kb][k2] = x;
-            }
+        if (t + 1 < wn) {
+            f32x16 s[C::KB];
+            qk_tile<C>(s, kbuf(1 - PAR), koff, qf);
+            schedule_qk<C>();
+            if (need_mask(t + 1)) mask_tile<C>(s, (t + 1) * C::BC, qi, n_kv, h);
+            pv_tile<C>(o, vbuf(PAR), voff, pc);
+            softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c);
+            schedule_pv_softmax<C>();
+        } else {
+            pv_tile<C>(o, vbuf(PAR), voff, pc);
         }
-
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + voff[db & 3] + 256 * (db >> 2);
-                    const i16x4 lo = lds_read_tr16(base);
-                    const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
-                    const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[db] = M::mma(a, pb[kb][k2], o[db]);
-                }
-            }
-        }
+    };
+    for (int t = 0; t < ntile; t += 2) {
+        iteration(std::integral_constant<int, 0>(), t, p0, p1);
+        if (t + 1 >= ntile) break;
+        iteration(std::integral_constant<int, 1>(), t + 1, p1, p0);
     }
 
     // ---- epilogue: O = O_acc / l, LSE = m + ln l ----
     if (qi >= n_q) return;
-    const float l_tot = l_acc + __shfl_xor(l_acc, 32);
+    const float l_tot = sum_halves(l_acc);
     const float inv = p.o_mul / l_tot;
     char *orow = p.o + ((int64_t)bh * n_q + qi) * C::RB;
 #pragma unroll
@@ -308,14 +427,14 @@ const Variant *variants16(int *count) {
         FA_V16(__bf16, FA_BF16, 64, 8, 64, 1),
         FA_V16(__bf16, FA_BF16, 128, 8, 64, 0),
         FA_V16(__bf16, FA_BF16, 128, 8, 64, 1),
-        FA_V16(__bf16, FA_BF16, 256, 4, 64, 0),
-        FA_V16(__bf16, FA_BF16, 256, 4, 64, 1),
+        FA_V16(__bf16, FA_BF16, 256, 4, 32, 0),
+        FA_V16(__bf16, FA_BF16, 256, 4, 32, 1),
         FA_V16(_Float16, FA_F16, 64, 8, 64, 0),
         FA_V16(_Float16, FA_F16, 64, 8, 64, 1),
         FA_V16(_Float16, FA_F16, 128, 8, 64, 0),
         FA_V16(_Float16, FA_F16, 128, 8, 64, 1),
-        FA_V16(_Float16, FA_F16, 256, 4, 64, 0),
-        FA_V16(_Float16, FA_F16, 256, 4, 64, 1),
+        FA_V16(_Float16, FA_F16, 256, 4, 32, 0),
+        FA_V16(_Float16, FA_F16, 256, 4, 32, 1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
