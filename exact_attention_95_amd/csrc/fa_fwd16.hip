@@ -56,10 +56,14 @@ template <> struct Mma16<_Float16> {
     }
 };
 
-template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_>
+// PRIO: 0 = all waves at the same issue priority; 1 = the first half of the
+// waves (one per SIMD) run at priority 1, so the two waves sharing a SIMD
+// drift apart and one's softmax overlaps the other's matrix products;
+// 2 = a wave raises its priority while it issues the S^T MFMAs.
+template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_, int PRIO_ = 0>
 struct Cfg {
     typedef T_ T;
-    static constexpr int D = D_, NW = NW_, BC = BC_, NT = NW * 64, BR = 32 * NW;
+    static constexpr int D = D_, NW = NW_, BC = BC_, NT = NW * 64, BR = 32 * NW, PRIO = PRIO_;
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int RB = D * 2;                      // LDS / global row bytes
     static constexpr int NC = RB / 16;                    // 16-byte chunks per row
@@ -89,24 +93,55 @@ template <class C> __device__ __forceinline__ int kswz(int r) { return (r / C::R
 // spreads over 16 different bank groups.
 template <class C> __device__ __forceinline__ int vswz(int r) { return 4 * ((r / C::RPB) & C::VX); }
 
-// Issues the direct-to-LDS copies of rows [t0, t0 + BC) of one head's K (or
-// V, with vswz) into one LDS buffer.  Rows past n_kv are clamped to the last
-// row (their scores are masked and their P entries are zero).
+// Per-lane part of the direct-to-LDS copies of one K (or V) tile: copy
+// instruction i of wave w moves chunks cb..cb+63 (cb = (i*NW + w)*64) of the
+// tile's LDS image; this lane's chunk is row r, physical chunk pc, so it
+// fetches logical chunk pc ^ swizzle(r) of row r.
 template <class C, bool IS_V>
-__device__ __forceinline__ void load_tile(const char *src, int t0, int n_kv, char *buf, int w,
-                                          int lane) {
-#pragma unroll
-    for (int i = 0; i < C::LDI; ++i) {
-        const int cb = (i * C::NW + w) * 64;  // first chunk of this wave's copy
-        const int chunk = cb + lane;
+struct CopyPlan {
+    // Offsets are kept in registers only when there are few of them; wide
+    // heads (many copies per wave, many live accumulators) recompute them.
+    static constexpr bool KEEP = C::LDI <= 2;
+    unsigned off[KEEP ? C::LDI : 1];  // byte offset of the fetched chunk within a full tile
+    __device__ __forceinline__ static unsigned offset(int i, int w, int lane, int *row) {
+        const int chunk = (i * C::NW + w) * 64 + lane;
         const int r = chunk / C::NC;
-        const int pc = chunk % C::NC;          // physical chunk in the LDS row
-        int gr = t0 + r;
-        gr = gr < n_kv ? gr : n_kv - 1;
+        const int pc = chunk % C::NC;
         const int sw = IS_V ? vswz<C>(r) : kswz<C>(r);
-        copy16_to_lds(src + (int64_t)gr * C::RB + 16 * (pc ^ sw), buf + cb * 16);
+        *row = r;
+        return (unsigned)(r * C::RB + 16 * (pc ^ sw));
     }
-}
+    __device__ __forceinline__ CopyPlan(int w, int lane) {
+        int r;
+        if (KEEP) {
+#pragma unroll
+            for (int i = 0; i < C::LDI; ++i) off[i] = offset(i, w, lane, &r);
+        }
+    }
+    // Issues the copies of rows [t0, t0 + BC) of one head into an LDS buffer.
+    // Rows past n_kv (only in the last, ragged tile) are clamped to the last
+    // row: their scores are masked and their P entries are zero.
+    __device__ __forceinline__ void issue(const char *src, int t0, int n_kv, char *buf, int w,
+                                          int lane) const {
+        if (t0 + C::BC <= n_kv) {
+            const char *tile = src + (int64_t)t0 * C::RB;
+#pragma unroll
+            for (int i = 0; i < C::LDI; ++i) {
+                int r;
+                const unsigned o = KEEP ? off[KEEP ? i : 0] : offset(i, w, lane, &r);
+                copy16_to_lds(tile + o, buf + (i * C::NW + w) * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::LDI; ++i) {
+                int r;
+                const unsigned o = offset(i, w, lane, &r);
+                const int gr = min(t0 + r, n_kv - 1);
+                copy16_to_lds(src + (int64_t)gr * C::RB + (o - r * C::RB), buf + (i * C::NW + w) * 1024);
+            }
+        }
+    }
+};
 
 // v_permlane32_swap(a, b) returns ([a_lo, b_lo], [a_hi, b_hi]) (lo = lanes
 // 0-31, hi = lanes 32-63).  With a = b = x every lane thus receives the lower
@@ -135,21 +170,22 @@ __device__ __forceinline__ float sum_halves(float x) {
     return lo + hi;
 }
 
-// S^T (32 keys x 32 queries per block) = K_tile Q^T.
+// S^T (32 keys x 32 queries per block) = K_tile Q^T.  The KB accumulation
+// chains are interleaved so that consecutive MFMAs are independent.
 template <class C>
 __device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const char *Ks, const int (&koff)[C::NKO],
                                         const typename Mma16<typename C::T>::v8 (&qf)[C::KS]) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-        s[kb] = (f32x16){};
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = (f32x16){};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
             const v8 a = *(const v8 *)(Ks + kb * 32 * C::RB + koff[ks & 7] + 256 * (ks >> 3));
             s[kb] = M::mma(a, qf[ks], s[kb]);
         }
-    }
 }
 
 // O^T += V_tile^T P^T.  Register r of S^T block kb holds key
@@ -162,11 +198,11 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[C::DB], const char *Vs, cons
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
+            for (int db = 0; db < C::DB; ++db) {
                 const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + voff[db & 3] + 256 * (db >> 2);
                 const i16x4 lo = lds_read_tr16(base);
                 const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
@@ -194,8 +230,8 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[C::KB], int t0, int qi, in
 // more than TAU (wave-uniform decision, returned in `raised` with the factor
 // alpha that O must still be multiplied by), and writes P = exp2(S c - m_use)
 // as the MFMA operand type into pb while accumulating this half-wave's share
-// of the row sum (of the float32 P, before rounding) into l_acc.  c > 0, so masked scores
-// (-inf) give P = 0.
+// of the row sum (of the float32 P, before rounding) into l_acc.  c > 0, so
+// masked scores (-inf) give P = 0.
 template <class C>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
                                              typename Mma16<typename C::T>::v8 (&pb)[C::KB][2],
@@ -220,15 +256,14 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -mref));
-            l4[r & 3] += s[kb][r];
-        }
-#pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             v8 x;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (T)s[kb][8 * k2 + e];
+            for (int e = 0; e < 8; ++e) {
+                const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * k2 + e], c, -mref));
+                l4[e & 3] += v;
+                x[e] = (T)v;
+            }
             pb[kb][k2] = x;
         }
     }
@@ -242,9 +277,11 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
 // are in flight at a time.
 template <class C>
 __device__ __forceinline__ void schedule_qk() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+    constexpr int N = C::KB * C::KS;
+    constexpr int AHEAD = N < 4 ? N : 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS read
 #pragma unroll
-    for (int i = 0; i < C::KB * C::KS; ++i) {
+    for (int i = 0; i < N; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -254,7 +291,7 @@ __device__ __forceinline__ void schedule_pv_softmax() {
     constexpr int NPV = C::DB * C::KB * 2;
     constexpr int VALU = 120 * C::KB / 2;  // softmax VALU instructions, about
     constexpr int VPM = (VALU + NPV - 1) / NPV;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -278,6 +315,7 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     const int w = wave_id();
     const int h = lane >> 5;     // half-wave
     const int l32 = lane & 31;
+    if (C::PRIO == 1 && w < C::NW / 2) __builtin_amdgcn_s_setprio(1);
 
     // ---- which (head, query block) ----
     const int bid = xcd_remap(blockIdx.x, p.n_wg);
@@ -303,9 +341,11 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
         return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
     };
 
-    load_tile<C, false>(kh, 0, n_kv, kbuf(0), w, lane);
-    load_tile<C, true>(vh, 0, n_kv, vbuf(0), w, lane);
-    if (ntile > 1) load_tile<C, false>(kh, C::BC, n_kv, kbuf(1), w, lane);
+    const CopyPlan<C, false> kplan(w, lane);
+    const CopyPlan<C, true> vplan(w, lane);
+    kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
+    vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);
+    if (ntile > 1) kplan.issue(kh, C::BC, n_kv, kbuf(1), w, lane);
 
     // ---- Q^T operand: lane holds Q[qi][ks*16 + 8h .. +7] for every k-step ----
     v8 qf[C::KS];
@@ -367,8 +407,8 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
         constexpr int PAR = decltype(par)::value;
         wait_vm();
         __syncthreads();
-        if (t + 2 < ntile) load_tile<C, false>(kh, (t + 2) * C::BC, n_kv, kbuf(PAR), w, lane);
-        if (t + 1 < ntile) load_tile<C, true>(vh, (t + 1) * C::BC, n_kv, vbuf(1 - PAR), w, lane);
+        if (t + 2 < ntile) kplan.issue(kh, (t + 2) * C::BC, n_kv, kbuf(PAR), w, lane);
+        if (t + 1 < ntile) vplan.issue(vh, (t + 1) * C::BC, n_kv, vbuf(1 - PAR), w, lane);
         if (t >= wn) return;
         if (raised) {
 #pragma unroll
@@ -376,9 +416,12 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
         }
         if (t + 1 < wn) {
             f32x16 s[C::KB];
+            const bool masked = need_mask(t + 1);
+            if (C::PRIO == 2) __builtin_amdgcn_s_setprio(1);
             qk_tile<C>(s, kbuf(1 - PAR), koff, qf);
             schedule_qk<C>();
-            if (need_mask(t + 1)) mask_tile<C>(s, (t + 1) * C::BC, qi, n_kv, h);
+            if (C::PRIO == 2) __builtin_amdgcn_s_setprio(0);
+            if (masked) mask_tile<C>(s, (t + 1) * C::BC, qi, n_kv, h);
             pv_tile<C>(o, vbuf(PAR), voff, pc);
             softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c);
             schedule_pv_softmax<C>();
@@ -419,6 +462,9 @@ int launch(const KParams &p, void *stream) {
 
 #define FA_V16(T, DT, D, NW, BC, CAUSAL)                                                   \
     Variant{DT, D, CAUSAL, 32 * NW, "br" #NW "x32_bc" #BC, &launch<Cfg<T, D, NW, BC, CAUSAL>>}
+#define FA_V16P(T, DT, D, NW, BC, CAUSAL, PRIO)                                            \
+    Variant{DT, D, CAUSAL, 32 * NW, "br" #NW "x32_bc" #BC "_prio" #PRIO,                   \
+            &launch<Cfg<T, D, NW, BC, CAUSAL, PRIO>>}
 
 // Host-side table of the compiled 16-bit variants.
 const Variant *variants16(int *count) {
@@ -435,6 +481,11 @@ const Variant *variants16(int *count) {
         FA_V16(_Float16, FA_F16, 128, 8, 64, 1),
         FA_V16(_Float16, FA_F16, 256, 4, 32, 0),
         FA_V16(_Float16, FA_F16, 256, 4, 32, 1),
+        FA_V16P(__bf16, FA_BF16, 128, 8, 64, 0, 1),
+        FA_V16P(__bf16, FA_BF16, 128, 8, 64, 0, 2),
+        FA_V16P(__bf16, FA_BF16, 64, 8, 64, 0, 1),
+        FA_V16(__bf16, FA_BF16, 64, 4, 64, 0),
+        FA_V16(__bf16, FA_BF16, 64, 8, 128, 0),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
