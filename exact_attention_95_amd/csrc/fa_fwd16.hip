@@ -56,14 +56,10 @@ template <> struct Mma16<_Float16> {
     }
 };
 
-// PRIO: 0 = all waves at the same issue priority; 1 = the first half of the
-// waves (one per SIMD) run at priority 1, so the two waves sharing a SIMD
-// drift apart and one's softmax overlaps the other's matrix products;
-// 2 = a wave raises its priority while it issues the S^T MFMAs.
-template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_, int PRIO_ = 0>
+template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_>
 struct Cfg {
     typedef T_ T;
-    static constexpr int D = D_, NW = NW_, BC = BC_, NT = NW * 64, BR = 32 * NW, PRIO = PRIO_;
+    static constexpr int D = D_, NW = NW_, BC = BC_, NT = NW * 64, BR = 32 * NW;
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int RB = D * 2;                      // LDS / global row bytes
     static constexpr int NC = RB / 16;                    // 16-byte chunks per row
@@ -315,7 +311,6 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     const int w = wave_id();
     const int h = lane >> 5;     // half-wave
     const int l32 = lane & 31;
-    if (C::PRIO == 1 && w < C::NW / 2) __builtin_amdgcn_s_setprio(1);
 
     // ---- which (head, query block) ----
     const int bid = xcd_remap(blockIdx.x, p.n_wg);
@@ -417,10 +412,8 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
         if (t + 1 < wn) {
             f32x16 s[C::KB];
             const bool masked = need_mask(t + 1);
-            if (C::PRIO == 2) __builtin_amdgcn_s_setprio(1);
             qk_tile<C>(s, kbuf(1 - PAR), koff, qf);
             schedule_qk<C>();
-            if (C::PRIO == 2) __builtin_amdgcn_s_setprio(0);
             if (masked) mask_tile<C>(s, (t + 1) * C::BC, qi, n_kv, h);
             pv_tile<C>(o, vbuf(PAR), voff, pc);
             softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c);
@@ -462,30 +455,26 @@ int launch(const KParams &p, void *stream) {
 
 #define FA_V16(T, DT, D, NW, BC, CAUSAL)                                                   \
     Variant{DT, D, CAUSAL, 32 * NW, "br" #NW "x32_bc" #BC, &launch<Cfg<T, D, NW, BC, CAUSAL>>}
-#define FA_V16P(T, DT, D, NW, BC, CAUSAL, PRIO)                                            \
-    Variant{DT, D, CAUSAL, 32 * NW, "br" #NW "x32_bc" #BC "_prio" #PRIO,                   \
-            &launch<Cfg<T, D, NW, BC, CAUSAL, PRIO>>}
-
 // Host-side table of the compiled 16-bit variants.
 const Variant *variants16(int *count) {
     static const Variant table[] = {
+        // default first: d = 64 streams 128-key tiles (twice the work per barrier)
+        FA_V16(__bf16, FA_BF16, 64, 8, 128, 0),
         FA_V16(__bf16, FA_BF16, 64, 8, 64, 0),
+        FA_V16(__bf16, FA_BF16, 64, 8, 128, 1),
         FA_V16(__bf16, FA_BF16, 64, 8, 64, 1),
         FA_V16(__bf16, FA_BF16, 128, 8, 64, 0),
         FA_V16(__bf16, FA_BF16, 128, 8, 64, 1),
         FA_V16(__bf16, FA_BF16, 256, 4, 32, 0),
         FA_V16(__bf16, FA_BF16, 256, 4, 32, 1),
+        FA_V16(_Float16, FA_F16, 64, 8, 128, 0),
         FA_V16(_Float16, FA_F16, 64, 8, 64, 0),
+        FA_V16(_Float16, FA_F16, 64, 8, 128, 1),
         FA_V16(_Float16, FA_F16, 64, 8, 64, 1),
         FA_V16(_Float16, FA_F16, 128, 8, 64, 0),
         FA_V16(_Float16, FA_F16, 128, 8, 64, 1),
         FA_V16(_Float16, FA_F16, 256, 4, 32, 0),
         FA_V16(_Float16, FA_F16, 256, 4, 32, 1),
-        FA_V16P(__bf16, FA_BF16, 128, 8, 64, 0, 1),
-        FA_V16P(__bf16, FA_BF16, 128, 8, 64, 0, 2),
-        FA_V16P(__bf16, FA_BF16, 64, 8, 64, 0, 1),
-        FA_V16(__bf16, FA_BF16, 64, 4, 64, 0),
-        FA_V16(__bf16, FA_BF16, 64, 8, 128, 0),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
