@@ -1,13 +1,314 @@
-// Attention forward for OCP E4M3 inputs on gfx950 (output bfloat16).
+// Attention forward for OCP E4M3 (8-bit float) inputs on gfx950; O in bfloat16.
+//
+// Same decomposition, online softmax and one-tile software pipeline as the
+// 16-bit kernel (one workgroup per (batch*head, 256 query rows), one wave per
+// 32 rows, S^T = K Q^T so each lane owns a query row, K and V double-buffered
+// in LDS by direct global->LDS copies), with both products on the 8-bit
+// matrix instruction v_mfma_f32_32x32x64_f8f6f4:
+//
+//   S^T = K Q^T        E4M3 codes; the descales of Q and K are folded into
+//                      the exponent factor c = |scale| dq dk log2(e)
+//   P = exp2(S c - m)  float32; the reference max follows every increase
+//                      (so P <= 1); the row sum l accumulates the float32 P
+//   O^T += V^T (256 P)^T  P scaled by 2^8 into E4M3's normal range and
+//                      rounded to E4M3; V read with ds_read_b64_tr_b8
+//   O = O_acc dv / (256 l)   stored as bfloat16
+//
+// Key order inside a 32-key block: row rho of the S^T MFMA is key
+// pi(rho) = 16 ((rho/4) % 2) + 4 (rho/8) + rho % 4, which makes the S^T
+// registers of each half-wave hold 16 consecutive keys, so the V^T operand
+// of the P V product is four transposed reads of 8 consecutive rows.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "../../include/fa.h"
 
 namespace fa {
+namespace {
+
+template <bool CAUSAL_>
+struct Cfg8 {
+    static constexpr int D = 128, NW = 8, BC = 64, NT = NW * 64, BR = 32 * NW;
+    static constexpr bool CAUSAL = CAUSAL_;
+    static constexpr int RB = D;            // bytes per row
+    static constexpr int TILE = BC * RB;    // 8 KB
+    static constexpr int LDS = 4 * TILE;    // K0, K1, V0, V1
+    static constexpr int KS = D / 64;       // k-steps of S^T = K Q^T
+    static constexpr int KB = BC / 32;
+    static constexpr int DB = D / 32;
+    static_assert(TILE == 1024 * NW, "one copy instruction per wave per tile");
+};
+
+// Key row of S^T MFMA row rho (within a 32-key block).
+__device__ __forceinline__ int key_of_row(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+
+// LDS swizzles (XOR on the 16-byte chunk index of a 128-byte row).
+// K: the 16 rows one half-wave reads together are {0..7, 16..23} (+8, +32k);
+// this XOR gives each of the 8 rows of one parity its own chunk.
+__device__ __forceinline__ int kswz8(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+// V: a half-wave's transposed reads cover 8 consecutive rows x 2 chunks.
+__device__ __forceinline__ int vswz8(int r) { return 2 * ((r >> 1) & 3); }
+
+// Issues the direct-to-LDS copy of rows [t0, t0 + BC) of one head (one 16-byte
+// chunk per lane, one instruction per wave); rows past n_kv are clamped.
+template <class C, bool IS_V>
+__device__ __forceinline__ void copy_tile(const char *src, int t0, int n_kv, char *buf, int w, int lane) {
+    const int chunk = w * 64 + lane;
+    const int r = chunk >> 3;
+    const int pc = chunk & 7;
+    const int gr = min(t0 + r, n_kv - 1);
+    const int lc = pc ^ (IS_V ? vswz8(r) : kswz8(r));
+    copy16_to_lds(src + (int64_t)gr * C::RB + 16 * lc, buf + w * 1024);
+}
+
+__device__ __forceinline__ void both_halves8(float x, float &lo, float &hi) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    unsigned v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "v"(u));
+    const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+    lo = __builtin_bit_cast(float, (unsigned)r[0]);
+    hi = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+__device__ __forceinline__ f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// S^T = K_tile Q^T for the 2 x 32-key blocks of a tile.
+template <class C>
+__device__ __forceinline__ void qk8(f32x16 (&s)[C::KB], const char *Ks, const int (&koff)[C::KS][2],
+                                    const i32x8 (&qf)[C::KS]) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            const u32x4 lo = *(const u32x4 *)(Ks + kb * 32 * C::RB + koff[ks][0]);
+            const u32x4 hi = *(const u32x4 *)(Ks + kb * 32 * C::RB + koff[ks][1]);
+            const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            s[kb] = mma8(a, qf[ks], s[kb]);
+        }
+}
+
+// O^T += V^T P^T.  k-slot e (0..31) of half-wave h carries key
+// 32 (e/16) + 16 h + e % 16; four transposed reads of 8 rows give V^T.
+template <class C>
+__device__ __forceinline__ void pv8(f32x16 (&o)[C::DB], const char *Vs, const int (&voff)[C::DB],
+                                    const i32x8 &pb) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+        i32x2v r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[u] = lds_read_tr8(Vs + (8 * (u & 1) + 32 * (u >> 1)) * C::RB + voff[db]);
+        const i32x8 a = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+        o[db] = mma8(a, pb, o[db]);
+    }
+}
+
+// Keys past n_kv and (causal) keys after qi become -inf.
+template <class C>
+__device__ __forceinline__ void mask8(f32x16 (&s)[C::KB], int t0, int qi, int n_kv, int h) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = t0 + 32 * kb + 16 * h + r;
+            const bool vis = key < n_kv && (!C::CAUSAL || key <= qi);
+            s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+}
+
+// Online-softmax step (plate 08 merge): the reference max follows every
+// increase of the row max, P = exp2(S c - m) <= 1, the float32 P is summed
+// into l_acc and 256 P is rounded to E4M3 into the P^T operand; `raised` and
+// alpha tell the caller to rescale O before accumulating this tile.
+template <class C>
+__device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m_use, float &l_acc,
+                                         float &alpha, bool &raised, float c) {
+    float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+    float lo, hi;
+    both_halves8(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), lo, hi);
+    const float mt = fmaxf(lo, hi) * c;
+    raised = __any(mt > m_use);
+    const float m_new = raised ? fmaxf(m_use, mt) : m_use;
+    alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
+    l_acc *= alpha;
+    m_use = m_new;
+    const float mref = (m_use == kNegInf) ? 0.f : m_use;
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w4 + e], c, -mref));
+                l4[e] += v[e];
+            }
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(256.f * v[0], 256.f * v[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(256.f * v[2], 256.f * v[3], word, true);
+            pb[4 * kb + w4] = word;
+        }
+    l_acc += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    auto kbuf = [&](int i) { return smem + i * C::TILE; };
+    auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
+
+    const int lane = lane_id();
+    const int w = wave_id();
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+
+    const int bid = xcd_remap(blockIdx.x, p.n_wg);
+    const int bh = bid / p.n_qblk;
+    int qb = bid - bh * p.n_qblk;
+    if (C::CAUSAL) qb = p.n_qblk - 1 - qb;
+    const int q0 = qb * C::BR;
+    const int wq0 = q0 + w * 32;
+    const int qi = wq0 + l32;
+    const int n_q = p.n_q, n_kv = p.n_kv;
+    const char *qh = p.q + (int64_t)bh * n_q * C::RB;
+    const char *kh = p.k + (int64_t)bh * n_kv * C::RB;
+    const char *vh = p.v + (int64_t)bh * n_kv * C::RB;
+
+    int ntile = (n_kv + C::BC - 1) / C::BC;
+    if (C::CAUSAL) ntile = min(ntile, min(q0 + C::BR - 1, n_q - 1) / C::BC + 1);
+    int wn = 0;
+    if (wq0 < n_q) wn = C::CAUSAL ? min(ntile, min(wq0 + 31, n_q - 1) / C::BC + 1) : ntile;
+    auto need_mask = [&](int t) {
+        return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
+    };
+
+    copy_tile<C, false>(kh, 0, n_kv, kbuf(0), w, lane);
+    copy_tile<C, true>(vh, 0, n_kv, vbuf(0), w, lane);
+    if (ntile > 1) copy_tile<C, false>(kh, C::BC, n_kv, kbuf(1), w, lane);
+
+    // Q^T operand: lane holds Q[qi][64 ks + 32 h .. +31] for each k-step.
+    i32x8 qf[C::KS];
+    {
+        const char *qrow = qh + (int64_t)min(qi, n_q - 1) * C::RB + 32 * h;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            u32x4 lo = *(const u32x4 *)(qrow + 64 * ks);
+            u32x4 hi = *(const u32x4 *)(qrow + 64 * ks + 16);
+            if (p.neg) {  // scale < 0: flip the sign bit of every code (exact)
+                lo ^= 0x80808080u;
+                hi ^= 0x80808080u;
+            }
+            qf[ks] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+    // K operand: row key_of_row(l32) of each 32-key block, chunks 4ks + 2h and +1.
+    int koff[C::KS][2];
+    {
+        const int r = key_of_row(l32);
+        const int sw = kswz8(r);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) koff[ks][s2] = r * C::RB + 16 * ((4 * ks + 2 * h + s2) ^ sw);
+    }
+    // V^T operand: in group g = lane/16, lane j addresses row 16h + j/2 (+ the
+    // read's base row) and columns 32 db + 16 (g % 2) + 8 (j % 2).
+    int voff[C::DB];
+    {
+        const int j = lane & 15;
+        const int row = 16 * h + (j >> 1);
+        const int x = vswz8(row) >> 1;
+        const int g2 = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) voff[db] = row * C::RB + 16 * (2 * (db ^ x) + g2) + 8 * (j & 1);
+    }
+
+    f32x16 o[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) o[db] = (f32x16){};
+    float m_use = kNegInf, l_acc = 0.f, alpha = 1.f;
+    bool raised = false;
+    const float c = p.c;
+    i32x8 p0, p1;
+
+    wait_vm();
+    __syncthreads();
+    if (wn > 0) {
+        f32x16 s[C::KB];
+        qk8<C>(s, kbuf(0), koff, qf);
+        if (need_mask(0)) mask8<C>(s, 0, qi, n_kv, h);
+        softmax8<C>(s, p0, m_use, l_acc, alpha, raised, c);
+        raised = false;
+    }
+
+    auto iteration = [&](auto par, int t, i32x8 &pc, i32x8 &pn) {
+        constexpr int PAR = decltype(par)::value;
+        wait_vm();
+        __syncthreads();
+        if (t + 2 < ntile) copy_tile<C, false>(kh, (t + 2) * C::BC, n_kv, kbuf(PAR), w, lane);
+        if (t + 1 < ntile) copy_tile<C, true>(vh, (t + 1) * C::BC, n_kv, vbuf(1 - PAR), w, lane);
+        if (t >= wn) return;
+        if (raised) {
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) o[db] *= alpha;
+        }
+        if (t + 1 < wn) {
+            f32x16 s[C::KB];
+            qk8<C>(s, kbuf(1 - PAR), koff, qf);
+            if (need_mask(t + 1)) mask8<C>(s, (t + 1) * C::BC, qi, n_kv, h);
+            pv8<C>(o, vbuf(PAR), voff, pc);
+            softmax8<C>(s, pn, m_use, l_acc, alpha, raised, c);
+        } else {
+            pv8<C>(o, vbuf(PAR), voff, pc);
+        }
+    };
+    for (int t = 0; t < ntile; t += 2) {
+        iteration(std::integral_constant<int, 0>(), t, p0, p1);
+        if (t + 1 >= ntile) break;
+        iteration(std::integral_constant<int, 1>(), t + 1, p1, p0);
+    }
+
+    float lo, hi;
+    both_halves8(l_acc, lo, hi);
+    const float l_tot = lo + hi;
+    if (qi >= n_q) return;
+    const float inv = p.o_mul / (256.f * l_tot);
+    char *orow = p.o + ((int64_t)bh * n_q + qi) * (2 * C::D);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(o[db][4 * jj + e] * inv);
+            *(bf16x4 *)(orow + 2 * (32 * db + 8 * jj + 4 * h)) = out;
+        }
+    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
+}
+
+template <class C>
+int launch8(const KParams &p, void *stream) {
+    hipLaunchKernelGGL(fwd8_kernel<C>, dim3(p.n_wg), dim3(C::NT), 0, (hipStream_t)stream, p);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace
 
 // Host-side table of the compiled E4M3 variants.
 const Variant *variants8(int *count) {
-    *count = 0;
-    return nullptr;
+    static const Variant table[] = {
+        Variant{FA_FP8_E4M3, 128, 0, 256, "br8x32_bc64", &launch8<Cfg8<false>>},
+        Variant{FA_FP8_E4M3, 128, 1, 256, "br8x32_bc64", &launch8<Cfg8<true>>},
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
 }
 
 }  // namespace fa

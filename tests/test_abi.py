@@ -131,6 +131,16 @@ def test_variant_table():
                 assert fa.fa_variant_name(dt, d, c, n + 1) == ""
                 assert fa.fa_variant_name(dt, d, c, 0) == ""
     assert fa.fa_num_variants(fa.FA_BF16, 96, 0) == 0
+    for c in (0, 1):
+        assert fa.fa_num_variants(fa.FA_FP8_E4M3, 128, c) >= 1
+        assert fa.fa_num_variants(fa.FA_FP8_E4M3, 64, c) == 0
+
+
+def test_fp8_validation():
+    assert fa.fa_validate(good_args(dtype=fa.FA_FP8_E4M3, d=128)) == fa.FA_OK
+    assert fa.fa_validate(good_args(dtype=fa.FA_FP8_E4M3, d=64)) == fa.FA_ERR_HEAD_DIM
+    assert fa.fa_validate(good_args(dtype=fa.FA_FP8_E4M3, d=128, descale_k=math.inf)) == fa.FA_ERR_SCALE
+    assert fa.fa_validate(good_args(dtype=fa.FA_FP8_E4M3, d=128, descale_q=1e30, descale_k=1e30)) == fa.FA_ERR_SCALE
 
 
 def test_fwd_refuses_cpu_tensors():

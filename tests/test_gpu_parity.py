@@ -39,6 +39,9 @@ SMALL = [
     (2, 1, 130, 77, 64, "f32", True),
     (1, 1, 100, 300, 128, "f32", False),
     (1, 1, 97, 97, 256, "f32", True),
+    (1, 2, 512, 512, 128, "fp8_e4m3", False),
+    (2, 1, 333, 200, 128, "fp8_e4m3", True),
+    (1, 1, 70, 900, 128, "fp8_e4m3", False),
 ]
 
 
@@ -72,6 +75,23 @@ def test_every_variant_matches_oracle(dt, d, causal):
         say("variant", fa.fa_variant_name(DT_CODE[dt], d, causal, v))
         err = full_parity(w, tile=v, x=x)
         assert_within(w, err, fa.fa_variant_name(DT_CODE[dt], d, causal, v))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_fp8_variant_matches_oracle(causal):
+    n = fa.fa_num_variants(fa.FA_FP8_E4M3, 128, causal)
+    assert n >= 1
+    w, x = random_problem(8, 1, 2, 333, 333, 128, "fp8_e4m3", causal)
+    for v in range(1, n + 1):
+        err = full_parity(w, tile=v, x=x)
+        assert_within(w, err, fa.fa_variant_name(fa.FA_FP8_E4M3, 128, causal, v))
+
+
+def test_fp8_negative_scale_and_descales():
+    w, x = random_problem(9, 1, 2, 260, 300, 128, "fp8_e4m3", False, scale=-0.3)
+    err = full_parity(w, x=x)
+    say(err)
+    assert_within(w, err)
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
@@ -157,6 +177,7 @@ FULL = [
     ("headline_bf16_n8192_d128", 256),
     ("headline_bf16_causal_n8192_d128", 256),
     ("large_head_bf16_n16384_d256", 128),
+    ("fp8_e4m3_n16384_d128", 256),
 ]
 
 
