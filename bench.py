@@ -57,48 +57,111 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, target_s: float = 12.0) -> dict:
-    """The fp64 oracle on a bounded row sample of the same workload."""
-    import oracle
-    from exact_attention_95_amd.inputs import boost_rows  # noqa: F401  (same generator)
-    rng = np.random.default_rng([w.seed_id, 7])
-    heads = rng.choice(w.B * w.H, size=min(4, w.B * w.H), replace=False)
-    per_row = 4.0 * w.n_kv * w.d  # non-causal rows; causal rows are sampled uniformly below
+def cpu_baseline(w, x, target_s: float = 15.0) -> dict:
+    """The fp64 oracle (as it stands) on a bounded row sample of the same workload.
 
-    def sample(n_rows):
-        per_head = max(1, n_rows // len(heads))
-        rows = np.concatenate([bh * w.n_q + rng.integers(0, w.n_q, per_head) for bh in heads])
-        return rows.astype(np.int64)
+    Rows are drawn uniformly without replacement over all B*H*N_q rows; a
+    sample grows from 1024 rows until one run takes about target_s seconds of
+    host time (capped at the whole workload); the last run is reported.
+    """
+    import oracle
+    rng = np.random.default_rng([w.seed_id, 7])
+    total = w.B * w.H * w.n_q
 
     def flops_of(rows):
         i = rows % w.n_q
-        if w.causal:
-            return float(np.sum(4.0 * np.minimum(i + 1, w.n_kv) * w.d))
-        return per_row * rows.size
+        vis = np.minimum(i + 1, w.n_kv) if w.causal else np.full(rows.shape, w.n_kv)
+        return float(np.sum(4.0 * vis * w.d))
 
     qo, ko, vo = x["q"], x["k"], x["v"]
     if w.dtype == "fp8_e4m3":
         dq, dk, dv = x["descale"]
         qo, ko, vo = (oracle.dequant_e4m3(t, s) for t, s in ((qo, dq), (ko, dk), (vo, dv)))
-    # calibrate on a small sample, then size the measured one to ~target_s
-    rows = sample(64)
-    t0 = time.perf_counter()
-    oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
-    dt = time.perf_counter() - t0
-    n = int(min(max(64, 64 * target_s / max(dt, 1e-3)), 200000))
-    rows = sample(n)
-    t0 = time.perf_counter()
-    oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
-    dt = time.perf_counter() - t0
+    # grow the sample until it takes about target_s (the per-call fp64 conversion
+    # of the touched heads is a fixed cost, so one calibration step undershoots)
+    n = min(1024, total)
+    while True:
+        rows = np.sort(rng.choice(total, size=n, replace=False))
+        t0 = time.perf_counter()
+        oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= 0.6 * target_s or n == total:
+            break
+        n = int(min(total, max(2 * n, n * target_s / max(dt, 1e-3))))
     f = flops_of(rows)
     return {
-        "value": f / dt / 1e12,
+        "value": round(f / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "%d query rows (uniform over %d heads) of workload %s, fp64 three-pass "
-                  "oracle, %.1f s, %.3g FLOP" % (rows.size, len(heads), w.name, dt, f),
+        "sample": "%d of %d query rows (uniform, without replacement) of workload %s; fp64 "
+                  "three-pass oracle, %.1f s, %.4g FLOP" % (rows.size, total, w.name, dt, f),
     }
+
+
+def summarize_counters(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per launch of the attention kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
+    counter reads for a plain 1 GiB device copy (hipMemcpy's copy kernel) run
+    in the same process (bench.py --copy-calibration)."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    def factor_and_value(path, counter):
+        rows = per_kernel(path, counter)
+        copy = [v for k, vals in rows.items() if "copyBuffer" in k for v in vals]
+        fa_vals = [v for k, vals in rows.items() if "fwd" in k and "fa" in k for v in vals]
+        if not copy or not fa_vals:
+            raise RuntimeError("missing copy or attention dispatches in %s" % path)
+        copy_kib = sorted(copy)[len(copy) // 2]
+        factor = (1 << 30) / (copy_kib * 1024.0)
+        value = sum(fa_vals) / len(fa_vals) * 1024.0
+        return factor, value
+
+    ff, fetch = factor_and_value(fetch_csv, "FETCH_SIZE")
+    wf, write = factor_and_value(write_csv, "WRITE_SIZE")
+    rec = {
+        "workload": workload,
+        "kernel_source_digest": kernel_source_digest(),
+        "fetch_bytes_raw": fetch, "fetch_factor": ff,
+        "write_bytes_raw": write, "write_factor": wf,
+        "hbm_bytes_per_launch": round(fetch * ff + write * wf),
+    }
+    return rec
+
+
+def memory_report(names) -> list:
+    """Device memory of fa_fwd (inputs, outputs and nothing else) against the
+    analytic footprint of materialising S and P (N x N each, input dtype)."""
+    import torch
+    from exact_attention_95_amd import fa
+    from exact_attention_95_amd.inputs import WORKLOADS, make_inputs
+    out = []
+    for name in names:
+        w = WORKLOADS[name]
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        x = make_inputs(w)
+        q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
+        del x
+        o, lse = fa.fwd(q, k, v, scale=w.sm_scale, causal=w.causal)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        esize = q.element_size()
+        tensors = (q.numel() + k.numel() + v.numel() + o.numel()) * esize + lse.numel() * 4
+        s_and_p = 2 * w.B * w.H * w.n_q * w.n_kv * esize
+        out.append({"workload": name, "device_bytes_peak": peak, "inputs_outputs_bytes": tensors,
+                    "materialised_s_p_bytes": s_and_p,
+                    "materialised_fits_288GB": bool(s_and_p + tensors < 288e9)})
+        del q, k, v, o, lse
+    return out
 
 
 def main(argv=None) -> int:
@@ -111,7 +174,21 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
+                         "counter_collection.csv files and exit")
+    ap.add_argument("--memory-report", action="store_true",
+                    help="print device memory of the long causal fp16 workloads vs a "
+                         "materialised N x N baseline and exit")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        rec = summarize_counters(args.workload, *args.summarize_counters)
+        path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % args.workload)
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the multi-GPU split (heads across GPUs, "
@@ -125,9 +202,14 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.memory_report:
+        for rec in memory_report(["long_f16_causal_n4096_d64", "long_f16_causal_n16384_d64",
+                                  "long_f16_causal_n65536_d64"]):
+            print(json.dumps(rec), flush=True)
+        return 0
+    w = WORKLOADS[args.workload]
     x = make_inputs(w)
     q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
     out_dtype = torch.bfloat16 if w.dtype == "fp8_e4m3" else q.dtype
@@ -164,6 +246,7 @@ def main(argv=None) -> int:
         return 1
 
     if args.copy_calibration:
+        # a plain device-to-device copy of exactly 1 GiB (hipMemcpy's copy kernel)
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
