@@ -31,6 +31,16 @@ METRIC = ("attention fwd TFLOP/s (4·B·H·N²·d) and % of MFMA peak, "
 DEFAULT_WORKLOAD = "headline_bf16_n8192_d128"
 # MI355X dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x flop/clk/CU of the matrix cores
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8_e4m3": 5033.2, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+ELEM_BYTES = {"bf16": 2, "f16": 2, "fp8_e4m3": 1, "f32": 4}
+
+
+def algorithmic_bytes(w) -> float:
+    """Q, K, V read once; O and LSE written once (bytes per launch)."""
+    e = ELEM_BYTES[w.dtype]
+    oe = 2 if w.dtype == "fp8_e4m3" else e
+    per_head = (w.n_q * w.d * e + 2 * w.n_kv * w.d * e + w.n_q * w.d * oe + w.n_q * 4)
+    return float(w.B * w.H * per_head)
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -171,6 +181,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--tile", type=int, default=0, help="fa_fwd_args.tile_override")
+    ap.add_argument("--splitkv", type=int, default=None,
+                    help="use the split-KV entry point with this many chunks (0: library "
+                         "choice); default: on for workloads with at most 16 query rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -221,11 +234,22 @@ def main(argv=None) -> int:
     st = fa.fa_validate(fargs)
     if st != fa.FA_OK:
         raise fa.FaError(st)
+    splitkv = args.splitkv if args.splitkv is not None else (0 if w.n_q <= 16 else None)
+    if splitkv is not None:
+        need = fa.fa_splitkv_workspace_bytes(fargs, splitkv)
+        if need < 0:
+            raise fa.FaError(fa.FA_ERR_VARIANT)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
-    def step():
-        s = fa.fa_fwd_ex(fargs)
-        if s != fa.FA_OK:
-            raise fa.FaError(s)
+        def step():
+            s = fa.fa_fwd_splitkv(fargs, splitkv, workspace.data_ptr(), workspace.numel())
+            if s != fa.FA_OK:
+                raise fa.FaError(s)
+    else:
+        def step():
+            s = fa.fa_fwd_ex(fargs)
+            if s != fa.FA_OK:
+                raise fa.FaError(s)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -256,8 +280,14 @@ def main(argv=None) -> int:
 
     flops = w.flops
     value = flops * args.steps / wall / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    nbytes = algorithmic_bytes(w)
+    # the bound of the dominant kernel: HBM when the arithmetic intensity is
+    # below the dtype's ridge point, else the matrix cores
+    hbm_bound = flops / nbytes < PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved, peak, unit = nbytes / (kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = flops / (kernel_ms * 1e-3) / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -273,10 +303,12 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.n_q, "N_kv": w.n_kv,
                    "d": w.d, "causal": w.causal, "dtype": w.dtype,
-                   "variant": fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1),
-                   "flops_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                   "variant": ("split_kv(%s)" % ("auto" if splitkv == 0 else splitkv)
+                               if splitkv is not None else
+                               fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1)),
+                   "flops_per_step": flops, "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": stored_traffic(w.name), "kernel_ms": round(kernel_ms, 4)},
     }
     if not args.no_cpu_baseline:

@@ -36,12 +36,13 @@ const Variant *variants(int *count) {
 
 namespace {
 
-const fa::Variant *find_variant(int dtype, int64_t d, int causal, int which) {
+const fa::Variant *find_variant(int dtype, int64_t d, int causal, int which, int split = 0) {
     int n = 0;
     const fa::Variant *t = fa::variants(&n);
     int seen = 0;
     for (int i = 0; i < n; ++i) {
-        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0)) {
+        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0) &&
+            t[i].split == split) {
             ++seen;
             if (seen == (which <= 0 ? 1 : which)) return &t[i];
         }
@@ -106,12 +107,19 @@ extern "C" int fa_validate(const fa_fwd_args *a) {
     return FA_OK;
 }
 
-extern "C" int fa_num_variants(int dtype, int64_t d, int causal) {
+namespace {
+int count_variants(int dtype, int64_t d, int causal, int split) {
     int n = 0, count = 0;
     const fa::Variant *t = fa::variants(&n);
     for (int i = 0; i < n; ++i)
-        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0)) ++count;
+        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0) && t[i].split == split)
+            ++count;
     return count;
+}
+}  // namespace
+
+extern "C" int fa_num_variants(int dtype, int64_t d, int causal) {
+    return count_variants(dtype, d, causal, 0);
 }
 
 extern "C" const char *fa_variant_name(int dtype, int64_t d, int causal, int v) {
@@ -132,7 +140,8 @@ extern "C" const char *fa_strerror(int status) {
         case FA_ERR_ALIAS: return "output overlaps an input or the other output";
         case FA_ERR_DEVICE: return "no usable gfx950 device";
         case FA_ERR_LAUNCH: return "kernel launch failed";
-        case FA_ERR_VARIANT: return "tile_override names no compiled variant";
+        case FA_ERR_VARIANT: return "no compiled variant for this problem (or tile_override out of range)";
+        case FA_ERR_WORKSPACE: return "split-KV workspace NULL, misaligned or too small";
         default: return "unknown status";
     }
 }
@@ -181,6 +190,10 @@ extern "C" int fa_fwd_ex(const fa_fwd_args *a) {
     p.c = fmaxf((float)score_factor(a), FLT_MIN);
     p.o_mul = a->dtype == FA_FP8_E4M3 ? a->descale_v : 1.0f;
     p.neg = a->scale < 0 ? 1 : 0;
+    p.n_split = 1;
+    p.kv_split = (int)a->N_kv;
+    p.part_o = nullptr;
+    p.part_lse = nullptr;
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours
     return v->launch(p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -207,4 +220,97 @@ extern "C" int fa_fwd(const void *Q, const void *K, const void *V, void *O, floa
     a.stream = nullptr;
     a.tile_override = 0;
     return fa_fwd_ex(&a);
+}
+
+namespace {
+
+// Chunking of the key range for split-KV: chunks of a whole number of 64-key
+// tiles, none empty.  Returns the number of chunks and sets *kv_split.
+const int kSplitTile = 64, kSplitRows = 128;  // key tile and query block of the split kernels
+
+int plan_splits(const fa_fwd_args *a, int num_splits, int *kv_split) {
+    const int64_t tiles = (a->N_kv + kSplitTile - 1) / kSplitTile;
+    const int64_t blocks = a->B * a->H * ((a->N_q + kSplitRows - 1) / kSplitRows);
+    int64_t want = num_splits;
+    if (want == 0) {
+        // about 1024 workgroups in flight (4 per CU), at least 4 tiles per chunk
+        want = (1024 + blocks - 1) / blocks;
+        const int64_t cap = tiles / 4 > 0 ? tiles / 4 : 1;
+        want = want < cap ? want : cap;
+    }
+    if (want > tiles) want = tiles;
+    if (want > 4096) want = 4096;
+    if (want < 1) want = 1;
+    const int64_t per = (tiles + want - 1) / want;
+    *kv_split = (int)(per * kSplitTile);
+    return (int)((a->N_kv + *kv_split - 1) / *kv_split);
+}
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Status of the split-KV arguments before the workspace is looked at.
+int validate_split(const fa_fwd_args *a, int num_splits) {
+    const int st = fa_validate(a);
+    if (st != FA_OK) return st;
+    if (num_splits < 0) return FA_ERR_SHAPE;
+    const int nv = count_variants(a->dtype, a->d, a->causal, 1);
+    if (nv == 0) return FA_ERR_VARIANT;
+    if (a->tile_override > nv) return FA_ERR_VARIANT;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int64_t fa_splitkv_workspace_bytes(const fa_fwd_args *a, int num_splits) {
+    if (validate_split(a, num_splits) != FA_OK) return -1;
+    if (a->B * a->H == 0 || a->N_q == 0) return 0;
+    int kv_split = 0;
+    const int64_t n = plan_splits(a, num_splits, &kv_split);
+    const int64_t rows = a->B * a->H * a->N_q;
+    return align256(n * rows * a->d * 4) + align256(n * rows * 4);
+}
+
+extern "C" int fa_fwd_splitkv(const fa_fwd_args *a, int num_splits, void *workspace,
+                              int64_t workspace_bytes) {
+    const int st = validate_split(a, num_splits);
+    if (st != FA_OK) return st;
+    if (a->B * a->H == 0 || a->N_q == 0) return FA_OK;
+    const int64_t need = fa_splitkv_workspace_bytes(a, num_splits);
+    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    const int64_t bh = a->B * a->H;
+    const int64_t qb = bh * a->N_q * a->d * in_size(a->dtype);
+    const int64_t kb = bh * a->N_kv * a->d * in_size(a->dtype);
+    const int64_t ob = bh * a->N_q * a->d * out_size(a->dtype);
+    const int64_t lb = a->LSE ? bh * a->N_q * 4 : 0;
+    if (overlap(workspace, need, a->Q, qb) || overlap(workspace, need, a->K, kb) ||
+        overlap(workspace, need, a->V, kb) || overlap(workspace, need, a->O, ob) ||
+        (lb && overlap(workspace, need, a->LSE, lb)))
+        return FA_ERR_ALIAS;
+    if (!device_ok()) return FA_ERR_DEVICE;
+    const fa::Variant *v = find_variant(a->dtype, a->d, a->causal, a->tile_override, 1);
+    if (!v) return FA_ERR_VARIANT;
+    int kv_split = 0;
+    const int n_split = plan_splits(a, num_splits, &kv_split);
+    const int64_t rows = bh * a->N_q;
+    fa::KParams p;
+    p.q = (const char *)a->Q;
+    p.k = (const char *)a->K;
+    p.v = (const char *)a->V;
+    p.o = (char *)a->O;
+    p.lse = a->LSE;
+    p.n_bh = (int)bh;
+    p.n_q = (int)a->N_q;
+    p.n_kv = (int)a->N_kv;
+    p.n_qblk = (int)((a->N_q + v->br - 1) / v->br);
+    p.n_wg = n_split * p.n_bh * p.n_qblk;
+    p.c = fmaxf((float)score_factor(a), FLT_MIN);
+    p.o_mul = 1.0f;
+    p.neg = a->scale < 0 ? 1 : 0;
+    p.n_split = n_split;
+    p.kv_split = kv_split;
+    p.part_o = (float *)workspace;
+    p.part_lse = (float *)((char *)workspace + align256((int64_t)n_split * rows * a->d * 4));
+    (void)hipGetLastError();
+    if (v->launch(p, a->stream) != 0) return FA_ERR_LAUNCH;
+    return fa::launch_merge(a->dtype, (int)a->d, p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -56,10 +56,16 @@ template <> struct Mma16<_Float16> {
     }
 };
 
-template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_>
+// SPLIT: the workgroup covers one chunk of the key range (split-KV) and
+// writes a float32 partial output and LSE instead of O.
+template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_, bool SPLIT_ = false>
 struct Cfg {
     typedef T_ T;
     static constexpr int D = D_, NW = NW_, BC = BC_, NT = NW * 64, BR = 32 * NW;
+    static constexpr bool SPLIT = SPLIT_;
+    // waves per SIMD the register budget must allow (the split kernels are
+    // bound by HBM and want two workgroups of 4 waves in flight per CU)
+    static constexpr int MIN_WAVES = SPLIT_ ? 2 : 1;
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int RB = D * 2;                      // LDS / global row bytes
     static constexpr int NC = RB / 16;                    // 16-byte chunks per row
@@ -297,7 +303,7 @@ __device__ __forceinline__ void schedule_pv_softmax() {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
+__global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     typedef typename C::T T;
     typedef Mma16<T> M;
     typedef typename M::v8 v8;
@@ -313,33 +319,53 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     const int l32 = lane & 31;
 
     // ---- which (head, query block) ----
-    const int bid = xcd_remap(blockIdx.x, p.n_wg);
+    int bid = xcd_remap(blockIdx.x, p.n_wg);
+    int split = 0;
+    if (C::SPLIT) {
+        const int per = p.n_bh * p.n_qblk;
+        split = bid / per;
+        bid -= split * per;
+    }
     const int bh = bid / p.n_qblk;
     int qb = bid - bh * p.n_qblk;
     if (C::CAUSAL) qb = p.n_qblk - 1 - qb;  // longest rows first
     const int q0 = qb * C::BR;
     const int wq0 = q0 + w * 32;             // first query row of this wave
     const int qi = wq0 + l32;                 // this lane's query row
-    const int n_q = p.n_q, n_kv = p.n_kv;
+    const int n_q = p.n_q;
+    // Keys [kofs, kofs + n_kv) of the head; the causal comparisons below use
+    // query indices shifted by -kofs so that they stay relative to this range.
+    const int kofs = C::SPLIT ? split * p.kv_split : 0;
+    const int n_kv = C::SPLIT ? min(p.kv_split, p.n_kv - kofs) : p.n_kv;
+    const int rq0 = q0 - kofs, rwq0 = wq0 - kofs, rqi = qi - kofs;
 
     const char *qh = p.q + (int64_t)bh * n_q * C::RB;
-    const char *kh = p.k + (int64_t)bh * n_kv * C::RB;
-    const char *vh = p.v + (int64_t)bh * n_kv * C::RB;
+    const char *kh = p.k + ((int64_t)bh * p.n_kv + kofs) * C::RB;
+    const char *vh = p.v + ((int64_t)bh * p.n_kv + kofs) * C::RB;
 
     // tiles streamed by the workgroup, and tiles this wave computes
     int ntile = (n_kv + C::BC - 1) / C::BC;
-    if (C::CAUSAL) ntile = min(ntile, min(q0 + C::BR - 1, n_q - 1) / C::BC + 1);
+    if (C::CAUSAL) {
+        const int last = min(q0 + C::BR - 1, n_q - 1) - kofs;  // last row, relative
+        ntile = last < 0 ? 0 : min(ntile, last / C::BC + 1);
+    }
     int wn = 0;
-    if (wq0 < n_q) wn = C::CAUSAL ? min(ntile, min(wq0 + 31, n_q - 1) / C::BC + 1) : ntile;
+    if (wq0 < n_q) {
+        const int last = min(wq0 + 31, n_q - 1) - kofs;
+        wn = !C::CAUSAL ? ntile : (last < 0 ? 0 : min(ntile, last / C::BC + 1));
+    }
+    (void)rq0;
     // tile t needs masking past n_kv, or when it reaches above this wave's first row
     auto need_mask = [&](int t) {
-        return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
+        return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > rwq0);
     };
 
     const CopyPlan<C, false> kplan(w, lane);
     const CopyPlan<C, true> vplan(w, lane);
-    kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
-    vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);
+    if (ntile > 0) {
+        kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
+        vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);
+    }
     if (ntile > 1) kplan.issue(kh, C::BC, n_kv, kbuf(1), w, lane);
 
     // ---- Q^T operand: lane holds Q[qi][ks*16 + 8h .. +7] for every k-step ----
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     if (wn > 0) {
         f32x16 s[C::KB];
         qk_tile<C>(s, kbuf(0), koff, qf);
-        if (need_mask(0)) mask_tile<C>(s, 0, qi, n_kv, h);
+        if (need_mask(0)) mask_tile<C>(s, 0, rqi, n_kv, h);
         softmax_tile<C>(s, p0, m_use, l_acc, alpha, raised, c);
         raised = false;  // O is still zero
     }
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
             const bool masked = need_mask(t + 1);
             qk_tile<C>(s, kbuf(1 - PAR), koff, qf);
             schedule_qk<C>();
-            if (masked) mask_tile<C>(s, (t + 1) * C::BC, qi, n_kv, h);
+            if (masked) mask_tile<C>(s, (t + 1) * C::BC, rqi, n_kv, h);
             pv_tile<C>(o, vbuf(PAR), voff, pc);
             softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c);
             schedule_pv_softmax<C>();
@@ -431,6 +457,24 @@ __global__ __launch_bounds__(C::NT) void fwd16_kernel(KParams p) {
     // ---- epilogue: O = O_acc / l, LSE = m + ln l ----
     if (qi >= n_q) return;
     const float l_tot = sum_halves(l_acc);
+    if (C::SPLIT) {
+        // partial of this key chunk, float32; a row that sees no key of the
+        // chunk (causal) gets O = 0 and LSE = -inf, i.e. weight 0 in the merge
+        const int64_t row = ((int64_t)split * p.n_bh + bh) * n_q + qi;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float *orow = p.part_o + row * C::D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = o[db][4 * jj + e] * inv;
+                *(f32x4 *)(orow + 32 * db + 8 * jj + 4 * h) = out;
+            }
+        if (h == 0) p.part_lse[row] = l_tot > 0.f ? (m_use + __log2f(l_tot)) * kLn2 : kNegInf;
+        return;
+    }
     const float inv = p.o_mul / l_tot;
     char *orow = p.o + ((int64_t)bh * n_q + qi) * C::RB;
 #pragma unroll
@@ -454,7 +498,55 @@ int launch(const KParams &p, void *stream) {
 }  // namespace
 
 #define FA_V16(T, DT, D, NW, BC, CAUSAL)                                                   \
-    Variant{DT, D, CAUSAL, 32 * NW, "br" #NW "x32_bc" #BC, &launch<Cfg<T, D, NW, BC, CAUSAL>>}
+    Variant{DT, D, CAUSAL, 0, 32 * NW, "br" #NW "x32_bc" #BC, &launch<Cfg<T, D, NW, BC, CAUSAL>>}
+#define FA_V16S(T, DT, D, NW, BC, CAUSAL)                                                  \
+    Variant{DT, D, CAUSAL, 1, 32 * NW, "split_br" #NW "x32_bc" #BC,                        \
+            &launch<Cfg<T, D, NW, BC, CAUSAL, true>>}
+// Merge of split-KV partials (Flash-Decoding's final step, "Flash Attention
+// 原理与实践" section 5.1), with the merge rule of "FlashAttention 与显存"
+// plate 08 applied to whole chunks: for each row, L = log sum_s exp(L_s) and
+// O = sum_s exp(L_s - L) O_s.  D/4 threads per row, four columns each.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void merge_kernel(KParams p) {
+    constexpr int TPR = D / 4;
+    const int64_t n_rows = (int64_t)p.n_bh * p.n_q;
+    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    if (row >= n_rows) return;
+    const int col = (threadIdx.x % TPR) * 4;
+    float mx = kNegInf;
+    for (int s = 0; s < p.n_split; ++s) mx = fmaxf(mx, p.part_lse[s * n_rows + row]);
+    float den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.n_split; ++s) {
+        const float ls = p.part_lse[s * n_rows + row];
+        const float wgt = ls == kNegInf ? 0.f : expf(ls - mx);
+        den += wgt;
+        acc += wgt * *(const f32x4 *)(p.part_o + (s * n_rows + row) * D + col);
+    }
+    const float inv = p.o_mul / den;
+    TO *orow = (TO *)p.o + row * D + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = (TO)(acc[e] * inv);
+    if (p.lse && col == 0) p.lse[row] = mx + logf(den);
+}
+
+template <typename TO, int D>
+int launch_merge_t(const KParams &p, void *stream) {
+    constexpr int RPB = 256 / (D / 4);
+    const int64_t n_rows = (int64_t)p.n_bh * p.n_q;
+    hipLaunchKernelGGL((merge_kernel<TO, D>), dim3((unsigned)((n_rows + RPB - 1) / RPB)), dim3(256), 0,
+                       (hipStream_t)stream, p);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int launch_merge(int dtype, int d, const KParams &p, void *stream) {
+    if (dtype == FA_BF16 && d == 64) return launch_merge_t<__bf16, 64>(p, stream);
+    if (dtype == FA_BF16 && d == 128) return launch_merge_t<__bf16, 128>(p, stream);
+    if (dtype == FA_F16 && d == 64) return launch_merge_t<_Float16, 64>(p, stream);
+    if (dtype == FA_F16 && d == 128) return launch_merge_t<_Float16, 128>(p, stream);
+    return 1;
+}
+
 // Host-side table of the compiled 16-bit variants.
 const Variant *variants16(int *count) {
     static const Variant table[] = {
@@ -475,6 +567,15 @@ const Variant *variants16(int *count) {
         FA_V16(_Float16, FA_F16, 128, 8, 64, 1),
         FA_V16(_Float16, FA_F16, 256, 4, 32, 0),
         FA_V16(_Float16, FA_F16, 256, 4, 32, 1),
+        // split-KV partial kernels (decode: few query rows, long key ranges)
+        FA_V16S(__bf16, FA_BF16, 64, 4, 64, 0),
+        FA_V16S(__bf16, FA_BF16, 64, 4, 64, 1),
+        FA_V16S(__bf16, FA_BF16, 128, 4, 64, 0),
+        FA_V16S(__bf16, FA_BF16, 128, 4, 64, 1),
+        FA_V16S(_Float16, FA_F16, 64, 4, 64, 0),
+        FA_V16S(_Float16, FA_F16, 64, 4, 64, 1),
+        FA_V16S(_Float16, FA_F16, 128, 4, 64, 0),
+        FA_V16S(_Float16, FA_F16, 128, 4, 64, 1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -152,7 +152,7 @@ int launch32(const KParams &p, void *stream) {
 
 }  // namespace
 
-#define FA_V32(D, NW, CAUSAL) Variant{FA_F32, D, CAUSAL, 32 * NW, "br" #NW "x32_bc32", &launch32<Cfg32<D, NW, CAUSAL>>}
+#define FA_V32(D, NW, CAUSAL) Variant{FA_F32, D, CAUSAL, 0, 32 * NW, "br" #NW "x32_bc32", &launch32<Cfg32<D, NW, CAUSAL>>}
 
 // Host-side table of the compiled float32 variants.
 const Variant *variants32(int *count) {

@@ -304,8 +304,8 @@ int launch8(const KParams &p, void *stream) {
 // Host-side table of the compiled E4M3 variants.
 const Variant *variants8(int *count) {
     static const Variant table[] = {
-        Variant{FA_FP8_E4M3, 128, 0, 256, "br8x32_bc64", &launch8<Cfg8<false>>},
-        Variant{FA_FP8_E4M3, 128, 1, 256, "br8x32_bc64", &launch8<Cfg8<true>>},
+        Variant{FA_FP8_E4M3, 128, 0, 0, 256, "br8x32_bc64", &launch8<Cfg8<false>>},
+        Variant{FA_FP8_E4M3, 128, 1, 0, 256, "br8x32_bc64", &launch8<Cfg8<true>>},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

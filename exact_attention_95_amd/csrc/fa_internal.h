@@ -21,6 +21,14 @@ struct KParams {
     float c;           // |scale| * log2(e) (times descale_q * descale_k for E4M3)
     float o_mul;       // factor applied to O at the end (descale_v for E4M3, else 1)
     int neg;           // 1 if scale < 0: Q is negated on load and c = |scale|*log2(e)
+    // split-KV (Flash-Decoding) only: the key range of every head is cut into
+    // n_split chunks of kv_split keys (the last one shorter, none empty); split
+    // s writes its normalised partial output and LSE (float32) to
+    // part_o[((s * n_bh + bh) * n_q + i) * d ...] and part_lse[(s * n_bh + bh) * n_q + i].
+    int n_split;
+    int kv_split;
+    float *part_o;
+    float *part_lse;
 };
 
 // A compiled kernel instance and the query-block height it uses.
@@ -30,13 +38,17 @@ struct Variant {
     int dtype;         // fa_dtype
     int d;             // head dimension
     int causal;        // 0 or 1
+    int split;         // 1: split-KV partial kernel (writes part_o / part_lse)
     int br;            // query rows per workgroup
     const char *name;
     launch_fn launch;
 };
 
-// Every compiled variant, grouped by (dtype, d, causal); within a group the
-// first entry is the default.
+// Every compiled variant, grouped by (dtype, d, causal, split); within a
+// group the first entry is the default.
 const Variant *variants(int *count);
+
+// Merge of split-KV partials into O (output dtype) and LSE; 0 on success.
+int launch_merge(int dtype, int d, const KParams &p, void *stream);
 
 }  // namespace fa

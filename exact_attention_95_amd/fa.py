@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_SCALE,
- FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT) = range(11)
+ FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE) = range(12)
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
-            "fa_variant_name")
+            "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes")
 
 
 class FaFwdArgs(ctypes.Structure):
@@ -72,6 +72,10 @@ def load(path: str = LIB_PATH):
             lib.fa_num_variants.argtypes = [ctypes.c_int, i64, ctypes.c_int]
             lib.fa_variant_name.restype = ctypes.c_char_p
             lib.fa_variant_name.argtypes = [ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
+            lib.fa_fwd_splitkv.restype = ctypes.c_int
+            lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int, vp, i64]
+            lib.fa_splitkv_workspace_bytes.restype = i64
+            lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int]
             _lib = lib
         return _lib
 
@@ -99,6 +103,14 @@ def fa_num_variants(dtype: int, d: int, causal: bool) -> int:
 
 def fa_variant_name(dtype: int, d: int, causal: bool, v: int) -> str:
     return load().fa_variant_name(dtype, d, int(bool(causal)), v).decode()
+
+
+def fa_fwd_splitkv(args: FaFwdArgs, num_splits: int, workspace, workspace_bytes: int) -> int:
+    return load().fa_fwd_splitkv(ctypes.byref(args), num_splits, workspace, workspace_bytes)
+
+
+def fa_splitkv_workspace_bytes(args: FaFwdArgs, num_splits: int) -> int:
+    return load().fa_splitkv_workspace_bytes(ctypes.byref(args), num_splits)
 
 
 def _dtype_code(t) -> int:
@@ -165,6 +177,43 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None,
     args = make_args(q, k, v, out, lse, scale, causal, descale or (1.0, 1.0, 1.0), stream, tile)
     with torch.cuda.device(q.device):
         st = fa_fwd_ex(args)
+    if st != FA_OK:
+        raise FaError(st)
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int = 0,
+                out=None, lse=None, with_lse: bool = True, stream=None, tile: int = 0,
+                workspace=None):
+    """Split-KV attention forward (bf16/fp16, d in {64, 128}); returns (O, LSE).
+
+    Same contract as ``fwd``; the key range is processed in ``num_splits``
+    chunks (0: library choice) whose partials are merged on the GPU.  The
+    float32 workspace is allocated with torch unless ``workspace`` (a uint8
+    device tensor) is given.
+    """
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise RuntimeError("fa.fwd_splitkv needs GPU tensors; there is no CPU path")
+    B, H, N_q, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if out is None:
+        out = torch.empty((B, H, N_q, d), dtype=q.dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args = make_args(q, k, v, out, lse, scale, causal, (1.0, 1.0, 1.0), stream, tile)
+    need = fa_splitkv_workspace_bytes(args, num_splits)
+    if need < 0:
+        raise FaError(fa_validate(args) or FA_ERR_VARIANT)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_splitkv(args, num_splits, workspace.data_ptr(), workspace.numel())
     if st != FA_OK:
         raise FaError(st)
     return out, lse

@@ -74,6 +74,8 @@ WORKLOADS = {
                  causal=True, boost_frac=0.01, boost=8.0),
         Workload("large_head_bf16_n16384_d256", 5, 2, 16, 16384, 16384, 256, "bf16"),
         Workload("fp8_e4m3_n16384_d128", 6, 2, 16, 16384, 16384, 128, "fp8_e4m3"),
+        # decode: one new query row per sequence against a long key/value cache
+        Workload("decode_bf16_b8_h32_nkv65536_d128", 7, 8, 32, 1, 65536, 128, "bf16"),
     ]
 }
 
@@ -95,10 +97,24 @@ def boost_rows(w: Workload) -> np.ndarray:
 
 
 def _tensor_f32(w: Workload, tensor_id: int, n: int) -> np.ndarray:
+    """All heads of one tensor; heads are drawn in parallel threads (each head
+    has its own generator, so the result does not depend on the schedule)."""
+    import concurrent.futures
+    import os
     x = np.empty((w.B, w.H, n, w.d), dtype=np.float32)
-    for b in range(w.B):
-        for h in range(w.H):
-            x[b, h] = head_normal(w.seed_id, tensor_id, b, h, n, w.d)
+
+    def fill(bh):
+        b, h = divmod(bh, w.H)
+        rng = np.random.default_rng([w.seed_id, tensor_id, b, h])
+        rng.standard_normal((n, w.d), dtype=np.float32, out=x[b, h])
+
+    if w.B * w.H * n * w.d < (1 << 22):
+        for bh in range(w.B * w.H):
+            fill(bh)
+    else:
+        workers = min(16, os.cpu_count() or 1)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, range(w.B * w.H)))
     return x
 
 

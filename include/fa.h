@@ -63,7 +63,8 @@ typedef enum {
     FA_ERR_ALIAS = 7,     /* O or LSE overlaps Q, K, V, or each other */
     FA_ERR_DEVICE = 8,    /* no usable gfx950 device / HIP runtime error before launch */
     FA_ERR_LAUNCH = 9,    /* the kernel launch failed */
-    FA_ERR_VARIANT = 10   /* tile_override names no compiled variant for this problem */
+    FA_ERR_VARIANT = 10,  /* no compiled variant for this problem / tile_override out of range */
+    FA_ERR_WORKSPACE = 11 /* split-KV workspace NULL, misaligned or too small */
 } fa_status;
 
 /*
@@ -113,6 +114,36 @@ int fa_fwd_ex(const fa_fwd_args *args);
  * return before launching.
  */
 int fa_validate(const fa_fwd_args *args);
+
+/*
+ * Split-KV forward (the decode-time scheme of "Flash Attention 原理与实践"
+ * section 5.1, Flash-Decoding): the key range of every (batch, head) is cut
+ * into num_splits contiguous chunks that separate workgroups process in
+ * parallel, each writing a float32 partial output O_s and LSE_s for its chunk
+ * into the caller's workspace; a second kernel then merges the chunks with
+ * the rule of "FlashAttention 与显存" plate 08 applied to whole chunks,
+ * L = ln sum_s exp(L_s), O = sum_s exp(L_s - L) O_s, and writes O and LSE as
+ * fa_fwd_ex does.  The result equals fa_fwd_ex's up to rounding; it pays off
+ * when B * H * ceil(N_q / 128) workgroups cannot fill the GPU (few query rows,
+ * long key ranges).
+ *
+ * args: as for fa_fwd_ex; dtype FA_BF16 or FA_F16 and d in {64, 128}
+ * (otherwise FA_ERR_VARIANT); tile_override 0 or 1.  num_splits: 0 lets the
+ * library choose, otherwise an upper bound (every chunk is non-empty, so
+ * fewer may be used).  workspace: device memory owned by the caller, 256-byte
+ * aligned, at least fa_splitkv_workspace_bytes(args, num_splits) bytes, not
+ * overlapping Q, K, V, O or LSE (FA_ERR_WORKSPACE / FA_ERR_ALIAS otherwise);
+ * its contents are overwritten.  Both kernels run on args->stream, in order.
+ */
+int fa_fwd_splitkv(const fa_fwd_args *args, int num_splits, void *workspace,
+                   int64_t workspace_bytes);
+
+/*
+ * Workspace bytes fa_fwd_splitkv needs for these arguments and num_splits
+ * (the same choice of chunks); 0 for an empty problem, -1 for arguments
+ * fa_fwd_splitkv would reject.  Host-only, no HIP call.
+ */
+int64_t fa_splitkv_workspace_bytes(const fa_fwd_args *args, int num_splits);
 
 /* Static, never-NULL description of a status code. */
 const char *fa_strerror(int status);

@@ -16,6 +16,9 @@ Functions and the passages they follow:
 * :func:`attention_blockwise` -- blockwise online softmax in v2 order
   ("FlashAttention算子优化" section 2, merge rule of plate 08) or v1 order
   ("Flash Attention 原理与实践" section 2.3).
+* :func:`merge` -- merge of per-chunk results over a key partition
+  (Flash-Decoding's last step, "Flash Attention 原理与实践" section 5.1, with
+  the merge rule of plate 08).
 * :func:`dequant_e4m3` -- OCP E4M3 code times a per-tensor descale.
 
 Pins (tests/test_oracle.py): brute force at 50 digits with mpmath, the
@@ -80,6 +83,8 @@ def _declare(lib):
             _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64, _i64p,
             ctypes.c_int64, _dp, _dp]
+    lib.fa_oracle_merge.restype = ctypes.c_int
+    lib.fa_oracle_merge.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
     lib.fa_oracle_num_threads.restype = ctypes.c_int
     lib.fa_oracle_num_threads.argtypes = []
     lib.fa_oracle_e4m3_to_double.restype = ctypes.c_double
@@ -213,6 +218,21 @@ def attention_blockwise(q, k, v, scale: float, causal: bool = False,
             _ptr(o), _ptr(lse))
     if st:
         raise RuntimeError("blockwise oracle failed: %d" % st)
+    return o, lse
+
+
+def merge(o_parts, lse_parts, lib=None):
+    """Merges per-chunk (O_s, LSE_s) of a key partition (plate 08's rule on
+    whole chunks).  o_parts: [n_parts, n_rows, d]; lse_parts: [n_parts, n_rows]
+    (-inf: chunk with no visible key).  Returns (O [n_rows, d], LSE [n_rows])."""
+    lib = lib or load()
+    op = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lp = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    n_parts, n_rows, d = op.shape
+    o = np.empty((n_rows, d))
+    lse = np.empty(n_rows)
+    if lib.fa_oracle_merge(_ptr(op), _ptr(lp), n_parts, n_rows, d, _ptr(o), _ptr(lse)):
+        raise RuntimeError("merge failed")
     return o, lse
 
 

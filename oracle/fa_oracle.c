@@ -288,6 +288,41 @@ int fa_oracle_blockwise_v1(const double *q, const double *k, const double *v,
 }
 
 /*
+ * Merge of partial results computed over a partition of the key range (the
+ * final step of Flash-Decoding, "Flash Attention 原理与实践" section 5.1):
+ * the merge rule of plate 08 applied to whole chunks.  With L_s the LSE and
+ * O_s the normalised output of chunk s for one row,
+ *   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s
+ * (computed against M = max_s L_s).  A chunk with no visible key has
+ * L_s = -inf and weight 0; a row with no visible key in any chunk is an error.
+ * o_parts: [n_parts, n_rows, d], lse_parts: [n_parts, n_rows]; o: [n_rows, d],
+ * lse: [n_rows].
+ */
+int fa_oracle_merge(const double *o_parts, const double *lse_parts, int64_t n_parts,
+                    int64_t n_rows, int64_t d, double *o, double *lse)
+{
+    if (!o_parts || !lse_parts || !o || !lse || n_parts < 1 || n_rows < 0 || d < 1) return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        double m = -INFINITY;
+        for (int64_t s = 0; s < n_parts; ++s)
+            if (lse_parts[s * n_rows + r] > m) m = lse_parts[s * n_rows + r];
+        if (m == -INFINITY) return 1;
+        double den = 0.0;
+        for (int64_t c = 0; c < d; ++c) o[r * d + c] = 0.0;
+        for (int64_t s = 0; s < n_parts; ++s) {
+            const double ls = lse_parts[s * n_rows + r];
+            if (ls == -INFINITY) continue;
+            const double w = exp(ls - m);
+            den += w;
+            for (int64_t c = 0; c < d; ++c) o[r * d + c] += w * o_parts[(s * n_rows + r) * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c) o[r * d + c] /= den;
+        lse[r] = m + log(den);
+    }
+    return 0;
+}
+
+/*
  * OCP 8-bit floating point E4M3 ("fn" variant) to double: 1 sign bit,
  * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
  * subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN and there are no

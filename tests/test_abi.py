@@ -148,3 +148,19 @@ def test_fwd_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(RuntimeError, match="GPU"):
         fa.fwd(q, q, q)
+
+
+def test_splitkv_workspace_bytes():
+    a = good_args(B=2, H=3, N_q=5, N_kv=1000, d=128, K=0x1000000, V=0x2000000, O=0x3000000,
+                  LSE=0x4000000)
+    # 1000 keys = 16 tiles of 64; 2 chunks of 8 tiles
+    n, rows = 2, 2 * 3 * 5
+    want = -(-n * rows * 128 * 4 // 256) * 256 + -(-n * rows * 4 // 256) * 256
+    assert fa.fa_splitkv_workspace_bytes(a, 2) == want
+    assert fa.fa_splitkv_workspace_bytes(a, 1000) > 0           # capped at one chunk per tile
+    assert fa.fa_splitkv_workspace_bytes(a, 0) > 0
+    assert fa.fa_splitkv_workspace_bytes(a, -1) == -1
+    assert fa.fa_splitkv_workspace_bytes(good_args(d=256), 0) == -1
+    assert fa.fa_splitkv_workspace_bytes(good_args(dtype=fa.FA_F32), 0) == -1
+    assert fa.fa_splitkv_workspace_bytes(good_args(B=0), 0) == 0
+    assert fa.fa_fwd_splitkv(good_args(B=0), 0, None, 0) == fa.FA_OK

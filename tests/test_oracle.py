@@ -236,6 +236,35 @@ def test_e4m3_decoder_against_torch():
     assert np.array_equal(deq, ref[:127] * d)
 
 
+def test_merge_of_key_chunks_equals_full_row():
+    """Attention over each chunk of a key partition, merged, equals attention
+    over all keys (Flash-Decoding's split and merge)."""
+    rng = np.random.default_rng(14)
+    n_q, n_kv, d = 9, 300, 16
+    q = rng.standard_normal((n_q, d)) * 2
+    k, v = rng.standard_normal((n_kv, d)), rng.standard_normal((n_kv, d))
+    o_ref, l_ref = oracle.attention(q, k, v, 0.4)
+    for _ in range(20):
+        cuts = np.unique(np.concatenate([[0, n_kv], rng.integers(1, n_kv, int(rng.integers(0, 12)))]))
+        parts = [oracle.attention(q, k[a:b], v[a:b], 0.4) for a, b in zip(cuts[:-1], cuts[1:])]
+        o, l = oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        assert np.abs(o - o_ref).max() <= 1e-12 and np.abs(l - l_ref).max() <= 1e-12
+
+
+def test_merge_ignores_empty_chunks_and_single_chunk_is_identity():
+    rng = np.random.default_rng(15)
+    o1, l1 = rng.standard_normal((1, 4, 8)), rng.standard_normal((1, 4))
+    o, l = oracle.merge(o1, l1)
+    assert np.array_equal(o, o1[0]) and np.abs(l - l1[0]).max() <= 1e-15
+    o2 = np.concatenate([o1, rng.standard_normal((1, 4, 8))])
+    l2 = np.concatenate([l1, np.full((1, 4), -np.inf)])
+    o, l = oracle.merge(o2, l2)
+    assert np.array_equal(o, o1[0]) and np.abs(l - l1[0]).max() <= 1e-15
+    # two equal chunks: same output, LSE + ln 2
+    o, l = oracle.merge(np.concatenate([o1, o1]), np.concatenate([l1, l1]))
+    assert np.abs(o - o1[0]).max() <= 1e-15 and np.abs(l - l1[0] - math.log(2)).max() <= 1e-14
+
+
 # ---- planted mistakes: each variant of the C source must fail a pin ----
 
 MUTATIONS = [
@@ -252,6 +281,8 @@ MUTATIONS = [
     ("v1 stale weight", "double old_w = (mi == -INFINITY) ? 0.0 : li * exp(mi - m_new);",
      "double old_w = (mi == -INFINITY) ? 0.0 : exp(mi - m_new);"),
     ("e4m3 bias", "else mag = ldexp(1.0 + mant / 8.0, e - 7);", "else mag = ldexp(1.0 + mant / 8.0, e - 8);"),
+    ("merge lse without max", "lse[r] = m + log(den);", "lse[r] = log(den);"),
+    ("merge unnormalised", "o[r * d + c] /= den;", "o[r * d + c] /= 1.0;"),
 ]
 
 
@@ -272,7 +303,13 @@ def _pins_pass(lib) -> bool:
         ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
         got = np.array([oracle.e4m3_to_double(c, lib=lib) for c in range(256)])
         ok = ~np.isnan(ref)
-        return bool(np.array_equal(ref[ok], got[ok]))
+        if not np.array_equal(ref[ok], got[ok]):
+            return False
+        q, k, v = _rand(rng, 4, 3), _rand(rng, 9, 3), _rand(rng, 9, 3)
+        o_ref, l_ref, _ = _mp_attention(q, k, v, 0.8, False)
+        parts = [oracle.attention(q, k[a:b], v[a:b], 0.8, lib=lib) for a, b in ((0, 4), (4, 9))]
+        o, l = oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]), lib=lib)
+        return bool(np.abs(o - o_ref).max() <= 1e-13 and np.abs(l - l_ref).max() <= 1e-13)
     except RuntimeError:
         return False
 
