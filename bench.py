@@ -44,17 +44,22 @@ def algorithmic_bytes(w) -> float:
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest() -> str:
-    """Hash of the kernel sources, to tell whether stored counters still apply."""
+KERNEL_SOURCE = {"f32": "fa_fwd32.hip", "f16": "fa_fwd16.hip", "bf16": "fa_fwd16.hip",
+                 "fp8_e4m3": "fa_fwd8.hip"}
+
+
+def kernel_source_digest(dtype: str) -> str:
+    """Hash of the sources that make the workload's kernel (its .hip file, the
+    shared device and launch code), to tell whether stored counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_95_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(["fa_device.h", "fa_internal.h", "fa_api.cpp", KERNEL_SOURCE[dtype]]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, dtype: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % workload)
@@ -62,7 +67,7 @@ def stored_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    if rec.get("kernel_source_digest") != kernel_source_digest(dtype):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -115,6 +120,7 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str) -> dict:
     counter reads for a plain 1 GiB device copy (hipMemcpy's copy kernel) run
     in the same process (bench.py --copy-calibration)."""
     import csv
+    from exact_attention_95_amd.inputs import WORKLOADS
 
     def per_kernel(path, counter):
         out = {}
@@ -138,7 +144,7 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str) -> dict:
     wf, write = factor_and_value(write_csv, "WRITE_SIZE")
     rec = {
         "workload": workload,
-        "kernel_source_digest": kernel_source_digest(),
+        "kernel_source_digest": kernel_source_digest(WORKLOADS[workload].dtype),
         "fetch_bytes_raw": fetch, "fetch_factor": ff,
         "write_bytes_raw": write, "write_factor": wf,
         "hbm_bytes_per_launch": round(fetch * ff + write * wf),
@@ -183,7 +189,7 @@ def main(argv=None) -> int:
     ap.add_argument("--tile", type=int, default=0, help="fa_fwd_args.tile_override")
     ap.add_argument("--splitkv", type=int, default=None,
                     help="use the split-KV entry point with this many chunks (0: library "
-                         "choice); default: on for workloads with at most 16 query rows")
+                         "choice, -1: off); default: on for workloads with at most 16 query rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -235,6 +241,8 @@ def main(argv=None) -> int:
     if st != fa.FA_OK:
         raise fa.FaError(st)
     splitkv = args.splitkv if args.splitkv is not None else (0 if w.n_q <= 16 else None)
+    if splitkv is not None and splitkv < 0:  # -1: force the single-pass entry point
+        splitkv = None
     if splitkv is not None:
         need = fa.fa_splitkv_workspace_bytes(fargs, splitkv)
         if need < 0:
@@ -309,7 +317,7 @@ def main(argv=None) -> int:
                    "flops_per_step": flops, "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": stored_traffic(w.name), "kernel_ms": round(kernel_ms, 4)},
+                     "traffic": stored_traffic(w.name, w.dtype), "kernel_ms": round(kernel_ms, 4)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, x)

@@ -39,6 +39,19 @@ __device__ __forceinline__ void copy16_to_lds(const void *gsrc, void *lds_wave_b
     __builtin_amdgcn_global_load_lds(gsrc, (FA_LDS void *)lds_wave_base, 16, 0, 0);
 }
 
+// Buffer resource for a byte range [base, base + bytes) (word 3 = 0x20000:
+// 32-bit raw data format, no stride, no swizzle).  Loads past `bytes` return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Asynchronous 16-byte copy from a buffer (SGPR base + 32-bit per-lane byte
+// offset) to LDS (buffer_load_dwordx4 ... lds); lane i writes to
+// lds_wave_base + 16 * i.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned voff, void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void *)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
 // Waits until every outstanding global load of this wave (including the
 // direct-to-LDS copies) has completed.
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

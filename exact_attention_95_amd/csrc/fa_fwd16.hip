@@ -78,7 +78,6 @@ struct Cfg {
     static constexpr int KB = BC / 32;                    // 32-key blocks per tile
     static constexpr int DB = D / 32;                     // 32-row blocks of O^T
     static constexpr int LDI = TILE / (1024 * NW);        // copy instructions per wave per tile
-    static constexpr int NKO = KS < 8 ? KS : 8;           // distinct K read offsets per lane
     static constexpr int NVO = DB < 4 ? DB : 4;           // distinct V read offsets per lane
     static constexpr float TAU = 8.0f;
     static_assert(TILE % (1024 * NW) == 0, "tile must split into whole wave copies");
@@ -120,26 +119,28 @@ struct CopyPlan {
             for (int i = 0; i < C::LDI; ++i) off[i] = offset(i, w, lane, &r);
         }
     }
-    // Issues the copies of rows [t0, t0 + BC) of one head into an LDS buffer.
-    // Rows past n_kv (only in the last, ragged tile) are clamped to the last
-    // row: their scores are masked and their P entries are zero.
+    // Issues the copies of rows [t0, t0 + BC) of one head into an LDS buffer,
+    // through a buffer resource that covers the head's rows [t0, n_kv).  Rows
+    // past n_kv (only in the last, ragged tile) are clamped to the last row:
+    // their scores are masked and their P entries are zero.
     __device__ __forceinline__ void issue(const char *src, int t0, int n_kv, char *buf, int w,
                                           int lane) const {
-        if (t0 + C::BC <= n_kv) {
-            const char *tile = src + (int64_t)t0 * C::RB;
+        const int rows = min(C::BC, n_kv - t0);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)t0 * C::RB, rows * C::RB);
+        if (rows == C::BC) {
 #pragma unroll
             for (int i = 0; i < C::LDI; ++i) {
                 int r;
                 const unsigned o = KEEP ? off[KEEP ? i : 0] : offset(i, w, lane, &r);
-                copy16_to_lds(tile + o, buf + (i * C::NW + w) * 1024);
+                copy16_to_lds(rs, o, buf + (i * C::NW + w) * 1024);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < C::LDI; ++i) {
                 int r;
                 const unsigned o = offset(i, w, lane, &r);
-                const int gr = min(t0 + r, n_kv - 1);
-                copy16_to_lds(src + (int64_t)gr * C::RB + (o - r * C::RB), buf + (i * C::NW + w) * 1024);
+                const int gr = min(r, rows - 1);
+                copy16_to_lds(rs, o - (unsigned)((r - gr) * C::RB), buf + (i * C::NW + w) * 1024);
             }
         }
     }
@@ -173,19 +174,26 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // S^T (32 keys x 32 queries per block) = K_tile Q^T.  The KB accumulation
-// chains are interleaved so that consecutive MFMAs are independent.
+// chains are interleaved so that consecutive MFMAs are independent.  koff0
+// is this lane's LDS offset of k-step 0; k-step ks (< 8) is at koff0 ^ 32 ks
+// (the swizzled chunk index is (2 ks + h) ^ kswz, and 2 ks occupies bits the
+// row offset and the half-wave bit leave free), plus 256 per further 8 steps.
+// The offsets are recomputed per tile (the empty asm keeps the compiler from
+// hoisting them into registers that live across the whole loop).
 template <class C>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const char *Ks, const int (&koff)[C::NKO],
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const char *Ks, int koff0,
                                         const typename Mma16<typename C::T>::v8 (&qf)[C::KS]) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
+    asm volatile("" : "+v"(koff0));
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) s[kb] = (f32x16){};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb) {
-            const v8 a = *(const v8 *)(Ks + kb * 32 * C::RB + koff[ks & 7] + 256 * (ks >> 3));
+            const int ko = (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3);
+            const v8 a = *(const v8 *)(Ks + kb * 32 * C::RB + ko);
             s[kb] = M::mma(a, qf[ks], s[kb]);
         }
 }
@@ -383,12 +391,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
 
     // ---- per-lane LDS offsets (tile-independent parts) ----
     // K operand of k-step ks: row l32 of the 32-key block, logical chunk 2ks+h.
-    int koff[C::NKO];
-    {
-        const int sw = kswz<C>(l32);
-#pragma unroll
-        for (int ks = 0; ks < C::NKO; ++ks) koff[ks] = l32 * C::RB + 16 * ((2 * ks + h) ^ sw);
-    }
+    const int koff = l32 * C::RB + 16 * (h ^ kswz<C>(l32));
     // V^T operand via transposed reads: the 16-lane group g = lane/16 covers
     // rows kbase + 4h + (lane%16)/4 and columns 32*dblk + 16*(g%2) + 4*(lane%4).
     int voff[C::NVO];

@@ -70,11 +70,14 @@ def test_single_head_f32_workload():
 def test_every_variant_matches_oracle(dt, d, causal):
     n = fa.fa_num_variants(DT_CODE[dt], d, causal)
     assert n >= 1
-    w, x = random_problem(7, 1, 2, 333, 333, d, dt, causal)
-    for v in range(1, n + 1):
-        say("variant", fa.fa_variant_name(DT_CODE[dt], d, causal, v))
-        err = full_parity(w, tile=v, x=x)
-        assert_within(w, err, fa.fa_variant_name(DT_CODE[dt], d, causal, v))
+    # tile counts: even with a ragged tail, odd, and a single tile
+    for seed, nq, nkv in ((7, 333, 333), (17, 200, 300), (27, 40, 50)):
+        w, x = random_problem(seed, 1, 2, nq, nkv, d, dt, causal)
+        for v in range(1, n + 1):
+            name = fa.fa_variant_name(DT_CODE[dt], d, causal, v)
+            say("variant", name, nq, nkv)
+            err = full_parity(w, tile=v, x=x)
+            assert_within(w, err, name)
 
 
 @pytest.mark.parametrize("causal", [False, True])
