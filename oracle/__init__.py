@@ -83,6 +83,10 @@ def _declare(lib):
             _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             ctypes.c_double, ctypes.c_int, _i64p, ctypes.c_int64, _i64p,
             ctypes.c_int64, _dp, _dp]
+    lib.fa_oracle_backward.restype = ctypes.c_int
+    lib.fa_oracle_backward.argtypes = [
+        _dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+        ctypes.c_int, _i64p, ctypes.c_int64, _i64p, ctypes.c_int64, _dp, _dp, _dp]
     lib.fa_oracle_merge.restype = ctypes.c_int
     lib.fa_oracle_merge.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
     lib.fa_oracle_num_threads.restype = ctypes.c_int
@@ -234,6 +238,53 @@ def merge(o_parts, lse_parts, lib=None):
     if lib.fa_oracle_merge(_ptr(op), _ptr(lp), n_parts, n_rows, d, _ptr(o), _ptr(lse)):
         raise RuntimeError("merge failed")
     return o, lse
+
+
+def backward(q, k, v, dout, scale: float, causal: bool = False, rows=None, keys=None, lib=None):
+    """Gradients dQ, dK, dV of standard attention in fp64 for upstream dO.
+
+    q, dout: [B,H,N_q,d]; k, v: [B,H,N_kv,d] (or one head [N,d]; numpy or CPU
+    torch, converted exactly to float64 one head at a time).  ``rows`` /
+    ``keys``: optional flat indices into B*H*N_q rows / B*H*N_kv keys; then
+    dQ is [len(rows), d] and dK, dV are [len(keys), d] (either may be an
+    empty selection).  Otherwise full [B,H,N,d] arrays are returned.
+    """
+    lib = lib or load()
+    q4, k4, v4, g4 = (_heads(t) for t in (q, k, v, dout))
+    B, H, n_q, d = q4.shape
+    n_kv = k4.shape[2]
+    if k4.shape != (B, H, n_kv, d) or v4.shape != (B, H, n_kv, d) or g4.shape != q4.shape:
+        raise ValueError("shape mismatch")
+    full = rows is None and keys is None
+    rows = np.arange(B * H * n_q, dtype=np.int64) if rows is None else np.asarray(rows, np.int64).ravel()
+    keys = np.arange(B * H * n_kv, dtype=np.int64) if keys is None else np.asarray(keys, np.int64).ravel()
+    dq = np.empty((rows.size, d))
+    dk = np.empty((keys.size, d))
+    dv = np.empty((keys.size, d))
+    for bh in np.unique(np.concatenate([rows // n_q, keys // n_kv])):
+        b, h = divmod(int(bh), H)
+        rsel = np.nonzero(rows // n_q == bh)[0]
+        ksel = np.nonzero(keys // n_kv == bh)[0]
+        lr = np.ascontiguousarray(rows[rsel] - bh * n_q)
+        lk = np.ascontiguousarray(keys[ksel] - bh * n_kv)
+        qh, kh, vh, gh = (_as_f64(t[b, h]) for t in (q4, k4, v4, g4))
+        dqh = np.empty((rsel.size, d))
+        dkh = np.empty((ksel.size, d))
+        dvh = np.empty((ksel.size, d))
+        st = lib.fa_oracle_backward(_ptr(qh), _ptr(kh), _ptr(vh), _ptr(gh), n_q, n_kv, d,
+                                    float(scale), int(bool(causal)), _ptr(lr, _i64p), rsel.size,
+                                    _ptr(lk, _i64p), ksel.size, _ptr(dqh), _ptr(dkh), _ptr(dvh))
+        if st:
+            raise RuntimeError("fa_oracle_backward failed: %d" % st)
+        dq[rsel], dk[ksel], dv[ksel] = dqh, dkh, dvh
+    if not full:
+        return dq, dk, dv
+    dq = dq.reshape(B, H, n_q, d)
+    dk = dk.reshape(B, H, n_kv, d)
+    dv = dv.reshape(B, H, n_kv, d)
+    if q.ndim == 2:
+        return dq[0, 0], dk[0, 0], dv[0, 0]
+    return dq, dk, dv
 
 
 def e4m3_to_double(code: int, lib=None) -> float:

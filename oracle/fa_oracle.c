@@ -1,5 +1,5 @@
 /*
- * CPU oracle for exact scaled-dot-product attention (forward).
+ * CPU oracle for exact scaled-dot-product attention (forward and gradients).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this file's library.  It shares no
@@ -320,6 +320,130 @@ int fa_oracle_merge(const double *o_parts, const double *lse_parts, int64_t n_pa
         lse[r] = m + log(den);
     }
     return 0;
+}
+
+/*
+ * Gradients of standard attention for one (batch, head) slice (the backward
+ * pass of "FlashAttention 与显存" plate 09, which keeps only O and per-row
+ * statistics and recomputes the rest).  The pages give no derivative
+ * formulas; these are the textbook ones for O = softmax(S) V with
+ * S = scale * Q K^T (rows masked as in the forward):
+ *   P_ij  = exp(s_ij - m_i) / l_i            (the forward's probabilities)
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij dP_ij                  (softmax Jacobian term)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale sum_j dS_ij k_j
+ *   dK_j  = scale sum_i dS_ij q_i
+ * for visible (i, j) only.  Computed in three plain passes:
+ *   pass 1, every row i: s_ij, m_i, l_i, P_ij, dP_ij, D_i (kept: m, l, D);
+ *   pass 2, selected rows: dQ_i (s_ij, dP_ij recomputed);
+ *   pass 3, selected keys: dV_j and dK_j over the rows that see key j.
+ * q, dout: [n_q, d]; k, v: [n_kv, d].  rows/keys: indices of the rows of dq
+ * and keys of dk/dv to produce (NULL: all, then n_rows = n_q, n_keys = n_kv).
+ * dq: [n_rows, d]; dk, dv: [n_keys, d].  Any of dq, dk, dv may be NULL.
+ */
+int fa_oracle_backward(const double *q, const double *k, const double *v, const double *dout,
+                       int64_t n_q, int64_t n_kv, int64_t d, double scale, int causal,
+                       const int64_t *rows, int64_t n_rows, const int64_t *keys, int64_t n_keys,
+                       double *dq, double *dk, double *dv)
+{
+    if (!q || !k || !v || !dout || n_q < 0 || n_kv < 1 || d < 1 || n_rows < 0 || n_keys < 0) return 1;
+    if ((!rows && n_rows != n_q) || (!keys && n_keys != n_kv)) return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= n_q) return 1;
+    }
+    for (int64_t r = 0; r < n_keys; ++r) {
+        int64_t j = keys ? keys[r] : r;
+        if (j < 0 || j >= n_kv) return 1;
+    }
+    double *m = (double *)malloc((size_t)(n_q ? n_q : 1) * sizeof(double));
+    double *l = (double *)malloc((size_t)(n_q ? n_q : 1) * sizeof(double));
+    double *D = (double *)malloc((size_t)(n_q ? n_q : 1) * sizeof(double));
+    if (!m || !l || !D) {
+        free(m); free(l); free(D);
+        return 2;
+    }
+    int status = 0;
+    /* pass 1: row statistics */
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)n_kv * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            status = 2;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < n_q; ++i) {
+            if (!s) continue;
+            const int64_t nv = visible_keys(i, n_kv, causal);
+            double mi = -INFINITY;
+            for (int64_t j = 0; j < nv; ++j) {
+                s[j] = score(q + i * d, k + j * d, d, scale);
+                if (s[j] > mi) mi = s[j];
+            }
+            double li = 0.0;
+            for (int64_t j = 0; j < nv; ++j) li += exp(s[j] - mi);
+            double Di = 0.0;
+            for (int64_t j = 0; j < nv; ++j) {
+                const double pij = exp(s[j] - mi) / li;
+                double dpij = 0.0;
+                for (int64_t c = 0; c < d; ++c) dpij += dout[i * d + c] * v[j * d + c];
+                Di += pij * dpij;
+            }
+            m[i] = mi;
+            l[i] = li;
+            D[i] = Di;
+        }
+        free(s);
+    }
+    /* pass 2: dQ of the selected rows */
+    if (!status && dq) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            const int64_t i = rows ? rows[r] : r;
+            const int64_t nv = visible_keys(i, n_kv, causal);
+            double *dqi = dq + r * d;
+            for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+            for (int64_t j = 0; j < nv; ++j) {
+                const double pij = exp(score(q + i * d, k + j * d, d, scale) - m[i]) / l[i];
+                double dpij = 0.0;
+                for (int64_t c = 0; c < d; ++c) dpij += dout[i * d + c] * v[j * d + c];
+                const double dsij = pij * (dpij - D[i]);
+                for (int64_t c = 0; c < d; ++c) dqi[c] += dsij * k[j * d + c];
+            }
+            for (int64_t c = 0; c < d; ++c) dqi[c] *= scale;
+        }
+    }
+    /* pass 3: dK and dV of the selected keys */
+    if (!status && (dk || dv)) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t r = 0; r < n_keys; ++r) {
+            const int64_t j = keys ? keys[r] : r;
+            double *dkj = dk ? dk + r * d : NULL;
+            double *dvj = dv ? dv + r * d : NULL;
+            for (int64_t c = 0; c < d; ++c) {
+                if (dkj) dkj[c] = 0.0;
+                if (dvj) dvj[c] = 0.0;
+            }
+            for (int64_t i = 0; i < n_q; ++i) {
+                if (j >= visible_keys(i, n_kv, causal)) continue;
+                const double pij = exp(score(q + i * d, k + j * d, d, scale) - m[i]) / l[i];
+                double dpij = 0.0;
+                for (int64_t c = 0; c < d; ++c) dpij += dout[i * d + c] * v[j * d + c];
+                const double dsij = pij * (dpij - D[i]);
+                for (int64_t c = 0; c < d; ++c) {
+                    if (dvj) dvj[c] += pij * dout[i * d + c];
+                    if (dkj) dkj[c] += dsij * q[i * d + c];
+                }
+            }
+            if (dkj)
+                for (int64_t c = 0; c < d; ++c) dkj[c] *= scale;
+        }
+    }
+    free(m); free(l); free(D);
+    return status;
 }
 
 /*
