@@ -314,3 +314,102 @@ extern "C" int fa_fwd_splitkv(const fa_fwd_args *a, int num_splits, void *worksp
     if (v->launch(p, a->stream) != 0) return FA_ERR_LAUNCH;
     return fa::launch_merge(a->dtype, (int)a->d, p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
+
+// ---------------------------------------------------------------------------
+// Backward.
+
+namespace {
+
+const fa::BwdVariant *find_bwd(int dtype, int64_t d, int causal) {
+    int n = 0;
+    const fa::BwdVariant *t = fa::bwd_variants(&n);
+    for (int i = 0; i < n; ++i)
+        if (t[i].dtype == dtype && t[i].d == d && t[i].causal == (causal ? 1 : 0)) return &t[i];
+    return nullptr;
+}
+
+const int kBwdKeyBlock = 128;  // keys per workgroup of the dK/dV kernel
+
+}  // namespace
+
+extern "C" int fa_bwd_validate(const fa_bwd_args *a) {
+    if (!a) return FA_ERR_NULL;
+    if (a->dtype != FA_BF16 && a->dtype != FA_F16) return FA_ERR_DTYPE;
+    if (a->d != 64 && a->d != 128) return FA_ERR_HEAD_DIM;
+    if (a->B < 0 || a->H < 0 || a->N_q < 0 || a->N_kv < 1) return FA_ERR_SHAPE;
+    if (a->N_q > kMaxRows || a->N_kv > kMaxRows) return FA_ERR_SHAPE;
+    if (a->B > 0 && a->H > INT32_MAX / a->B) return FA_ERR_SHAPE;
+    const int64_t bh = a->B * a->H;
+    if (bh > 0 && (a->N_q > INT64_MAX / 4 / a->d / bh || a->N_kv > INT64_MAX / 4 / a->d / bh))
+        return FA_ERR_SHAPE;
+    if (bh > 0 && ((a->N_q + 31) / 32 > INT32_MAX / bh || (a->N_kv + kBwdKeyBlock - 1) / kBwdKeyBlock > INT32_MAX / bh))
+        return FA_ERR_SHAPE;
+    if (!isfinite(a->scale) || !isfinite((float)((double)a->scale * 1.4426950408889634)))
+        return FA_ERR_SCALE;
+    if (!find_bwd(a->dtype, a->d, a->causal)) return FA_ERR_HEAD_DIM;
+    if (bh == 0) return FA_OK;  // nothing to read or write
+    if (!a->K || !a->V || !a->dK || !a->dV) return FA_ERR_NULL;
+    const bool rows = a->N_q > 0;
+    if (rows && (!a->Q || !a->O || !a->dO || !a->LSE || !a->dQ)) return FA_ERR_NULL;
+    uintptr_t al = (uintptr_t)a->K | (uintptr_t)a->V | (uintptr_t)a->dK | (uintptr_t)a->dV;
+    if (rows) al |= (uintptr_t)a->Q | (uintptr_t)a->O | (uintptr_t)a->dO | (uintptr_t)a->dQ;
+    if (al & 15) return FA_ERR_ALIGN;
+    if (rows && ((uintptr_t)a->LSE & 3)) return FA_ERR_ALIGN;
+    const int64_t qb = rows ? bh * a->N_q * a->d * 2 : 0;
+    const int64_t kb = bh * a->N_kv * a->d * 2;
+    const int64_t lb = rows ? bh * a->N_q * 4 : 0;
+    const void *outs[3] = {a->dQ, a->dK, a->dV};
+    const int64_t osz[3] = {qb, kb, kb};
+    const void *ins[6] = {a->Q, a->K, a->V, a->O, a->dO, a->LSE};
+    const int64_t isz[6] = {qb, kb, kb, qb, qb, lb};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], osz[i], ins[j], isz[j])) return FA_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], osz[i], outs[j], osz[j])) return FA_ERR_ALIAS;
+    }
+    return FA_OK;
+}
+
+extern "C" int64_t fa_bwd_workspace_bytes(const fa_bwd_args *a) {
+    if (fa_bwd_validate(a) != FA_OK) return -1;
+    return align256(a->B * a->H * a->N_q * 4);
+}
+
+extern "C" int fa_bwd(const fa_bwd_args *a, void *workspace, int64_t workspace_bytes) {
+    const int st = fa_bwd_validate(a);
+    if (st != FA_OK) return st;
+    const int64_t bh = a->B * a->H;
+    if (bh == 0) return FA_OK;
+    const int64_t need = fa_bwd_workspace_bytes(a);
+    if (need > 0) {
+        if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+        const int64_t qb = bh * a->N_q * a->d * 2;
+        const int64_t kb = bh * a->N_kv * a->d * 2;
+        const void *bufs[9] = {a->Q, a->K, a->V, a->O, a->dO, a->LSE, a->dQ, a->dK, a->dV};
+        const int64_t sz[9] = {qb, kb, kb, qb, qb, bh * a->N_q * 4, qb, kb, kb};
+        for (int i = 0; i < 9; ++i)
+            if (overlap(workspace, need, bufs[i], sz[i])) return FA_ERR_ALIAS;
+    }
+    if (!device_ok()) return FA_ERR_DEVICE;
+    const fa::BwdVariant *v = find_bwd(a->dtype, a->d, a->causal);
+    if (!v) return FA_ERR_HEAD_DIM;
+    fa::BwdParams p;
+    p.q = (const char *)a->Q;
+    p.k = (const char *)a->K;
+    p.v = (const char *)a->V;
+    p.o = (const char *)a->O;
+    p.dout = (const char *)a->dO;
+    p.lse = a->LSE;
+    p.dq = (char *)a->dQ;
+    p.dk = (char *)a->dK;
+    p.dv = (char *)a->dV;
+    p.delta = (float *)workspace;
+    p.n_bh = (int)bh;
+    p.n_q = (int)a->N_q;
+    p.n_kv = (int)a->N_kv;
+    p.c = (float)((double)a->scale * 1.4426950408889634);
+    p.scale = a->scale;
+    (void)hipGetLastError();
+    return v->launch(p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}

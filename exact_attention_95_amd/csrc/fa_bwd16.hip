@@ -1,0 +1,420 @@
+// Attention backward for 16-bit inputs (bf16, fp16) on gfx950.
+//
+// "FlashAttention 与显存" plate 09: the backward pass keeps only O and the
+// per-row statistic (here the LSE) from the forward and recomputes the
+// scores and probabilities tile by tile.  With P_ij = exp(scale q_i.k_j -
+// LSE_i) and the textbook gradients of softmax(scale Q K^T) V,
+//
+//   D_i   = sum_c dO_ic O_ic                      bwd_delta_kernel
+//   dQ_i  = scale sum_j P_ij (dP_ij - D_i) k_j     bwd_dq_kernel (query blocks)
+//   dV_j  = sum_i P_ij dO_i                         bwd_dkdv_kernel (key blocks)
+//   dK_j  = scale sum_i P_ij (dP_ij - D_i) q_i
+//
+// with dP_ij = dO_i . v_j.  dQ and dK/dV are computed by separate kernels so
+// that every output element has exactly one writer (no atomics; results are
+// bitwise repeatable); the price is computing S and dP twice.
+//
+// Both kernels use the 32x32x16 MFMA layouts of the forward kernel (the
+// tile helpers of fa_tile16.h).  In the dQ kernel a wave owns 32 query rows,
+// as in the forward: S^T = K Q^T and dP^T = V dO^T have one query per lane,
+// and dQ^T += K^T dS^T reads K transposed from LDS.  In the dK/dV kernel a
+// wave owns 32 keys and the roles of queries and keys swap: S = Q K^T and
+// dP = dO V^T have one key per lane (Q and dO tiles streamed through LDS,
+// this wave's K and V rows in registers), and dV^T += dO^T P, dK^T += Q^T dS
+// read dO and Q transposed.  LSE_i and D_i vary along the accumulator's rows
+// there, so they are staged through LDS with the tiles.
+#include "fa_device.h"
+#include "fa_tile16.h"
+#include "../../include/fa.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdTile = 64;  // rows per streamed tile (keys for dQ, queries for dK/dV)
+
+template <typename T_, int D_, int NW_, bool CAUSAL_>
+struct CfgB {
+    typedef T_ T;
+    static constexpr int D = D_, NW = NW_, BC = kBwdTile, NT = NW * 64, BR = 32 * NW;
+    static constexpr bool CAUSAL = CAUSAL_;
+    static constexpr int RB = D * 2, NC = RB / 16, RPB = RB >= 256 ? 1 : 256 / RB;
+    static constexpr int KX = (NC < 16 ? NC : 16) - 1, VX = (NC / 4 < 4 ? NC / 4 : 4) - 1;
+    static constexpr int TILE = BC * RB;
+    static constexpr int KS = D / 16, KB = BC / 32, DB = D / 32, LDI = TILE / (1024 * NW);
+    static constexpr int NVO = DB < 4 ? DB : 4;
+    static constexpr int LDS = 4 * TILE + 2 * 512;  // two streams x two buffers, + LSE/D tiles
+    // wave count per SIMD the register budget must allow
+    static constexpr int MIN_WAVES = 1;
+    static_assert(TILE % (1024 * NW) == 0, "tile must split into whole wave copies");
+};
+
+// Per-lane LDS offsets of the two operand reads of a tile in the V-style
+// layout (vswz): row reads (k-step 0 of qk_tile; k-step ks is koff ^ 32 ks)
+// and transposed reads (pv_tile).
+template <class C>
+__device__ __forceinline__ int row_offset_v(int lane) {
+    const int l32 = lane & 31, h = lane >> 5;
+    return l32 * C::RB + 16 * (h ^ vswz<C>(l32));
+}
+template <class C>
+__device__ __forceinline__ void tr_offsets(int lane, int (&voff)[C::NVO]) {
+    const int h = lane >> 5;
+    const int j = lane & 15;
+    const int rsub = 4 * h + (j >> 2);
+    const int x = vswz<C>(j >> 2) >> 2;
+    const int y = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+#pragma unroll
+    for (int db = 0; db < C::NVO; ++db) voff[db] = rsub * C::RB + 16 * (4 * (db ^ x) + y) + 8 * (j & 1);
+}
+
+// This lane's row of a [n, d] slice as the 32x32x16 B operand (row r of the
+// wave's 32-row block, k-steps ks: elements ks*16 + 8h .. +7).
+template <class C>
+__device__ __forceinline__ void load_rows(const char *base, int row, int n,
+                                          typename Mma16<typename C::T>::v8 (&f)[C::KS], int h) {
+    typedef typename Mma16<typename C::T>::v8 v8;
+    const int r = row < n ? row : n - 1;
+    const char *p = base + (int64_t)r * C::RB + 16 * h;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) f[ks] = __builtin_bit_cast(v8, *(const u32x4 *)(p + 32 * ks));
+}
+
+// Stores rows of an O^T-layout accumulator (one row per lane, d columns)
+// times mul, converted to T.
+template <class C>
+__device__ __forceinline__ void store_rows(char *rowp, const f32x16 (&acc)[C::DB], float mul, int h) {
+    typedef typename Mma16<typename C::T>::v4 v4;
+    typedef typename C::T T;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            v4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (T)(acc[db][4 * jj + e] * mul);
+            *(v4 *)(rowp + 2 * (32 * db + 8 * jj + 4 * h)) = out;
+        }
+}
+
+// One 32-row block of qk_tile: s = A B with A the block's rows (LDS, row
+// reads from koff0) and B this lane's register row f.
+template <class C>
+__device__ __forceinline__ void qk_rows(f32x16 &s, const char *blk, int koff0,
+                                        const typename Mma16<typename C::T>::v8 (&f)[C::KS]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+    asm volatile("" : "+v"(koff0));
+    s = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const v8 a = *(const v8 *)(blk + (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3));
+        s = M::mma(a, f[ks], s);
+    }
+}
+
+// One 32-row block of pv_tile: o^T += A^T B with A the block's rows (LDS,
+// transposed reads) and B = pb (the block's accumulator rows as packed
+// operands, k2 = 0, 1).
+template <class C>
+__device__ __forceinline__ void pv_rows(f32x16 (&o)[C::DB], const char *blk, const int (&voff)[C::NVO],
+                                        const typename Mma16<typename C::T>::v8 (&pb)[2]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const char *base = blk + 16 * k2 * C::RB + voff[db & 3] + 256 * (db >> 2);
+            const i16x4 lo = lds_read_tr16(base);
+            const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+            const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[db] = M::mma(a, pb[k2], o[db]);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// D_i = sum_c dO_ic O_ic (float32), D/8 lanes per row, 8 elements each.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+    typedef T T8 __attribute__((ext_vector_type(8)));
+    constexpr int TPR = D / 8;
+    const int64_t n_rows = (int64_t)p.n_bh * p.n_q;
+    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int col = (threadIdx.x % TPR) * 8;
+    float acc = 0.f;
+    if (row < n_rows) {
+        const T8 a = __builtin_bit_cast(T8, *(const u32x4 *)(p.o + (row * D + col) * 2));
+        const T8 b = __builtin_bit_cast(T8, *(const u32x4 *)(p.dout + (row * D + col) * 2));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
+    if (row < n_rows && threadIdx.x % TPR == 0) p.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (batch*head, block of 32*NW query rows), streaming
+// K and V tiles of 64 keys.  K is stored in the V-style layout (read both by
+// rows and transposed), V in the K-style layout (read by rows only).
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p) {
+    typedef typename C::T T;
+    typedef Mma16<T> M;
+    typedef typename M::v8 v8;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    auto kbuf = [&](int i) { return smem + i * C::TILE; };
+    auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
+
+    const int lane = lane_id();
+    const int w = wave_id();
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int n_qblk = (p.n_q + C::BR - 1) / C::BR;
+    const int bid = xcd_remap(blockIdx.x, p.n_bh * n_qblk);
+    const int bh = bid / n_qblk;
+    int qb = bid - bh * n_qblk;
+    if (C::CAUSAL) qb = n_qblk - 1 - qb;  // longest rows first
+    const int q0 = qb * C::BR;
+    const int wq0 = q0 + 32 * w;
+    const int qi = wq0 + l32;
+    const int n_q = p.n_q, n_kv = p.n_kv;
+
+    const char *qh = p.q + (int64_t)bh * n_q * C::RB;
+    const char *gh = p.dout + (int64_t)bh * n_q * C::RB;
+    const char *kh = p.k + (int64_t)bh * n_kv * C::RB;
+    const char *vh = p.v + (int64_t)bh * n_kv * C::RB;
+
+    int ntile = (n_kv + C::BC - 1) / C::BC;
+    if (C::CAUSAL) ntile = min(ntile, min(q0 + C::BR - 1, n_q - 1) / C::BC + 1);
+    int wn = 0;
+    if (wq0 < n_q) wn = !C::CAUSAL ? ntile : min(ntile, min(wq0 + 31, n_q - 1) / C::BC + 1);
+
+    const CopyPlan<C, true> kplan(w, lane);   // V-style layout
+    const CopyPlan<C, false> vplan(w, lane);  // K-style layout
+    if (ntile > 0) {
+        kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
+        vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);
+    }
+
+    v8 qf[C::KS], gf[C::KS];
+    load_rows<C>(qh, qi, n_q, qf, h);
+    load_rows<C>(gh, qi, n_q, gf, h);
+    const int64_t row = (int64_t)bh * n_q + (qi < n_q ? qi : n_q - 1);
+    const float lse2 = p.lse[row] * kLog2e;
+    const float dlt = p.delta[row];
+    const float c = p.c;
+
+    const int koff_k = row_offset_v<C>(lane);
+    const int koff_v = l32 * C::RB + 16 * (h ^ kswz<C>(l32));
+    int voff[C::NVO];
+    tr_offsets<C>(lane, voff);
+
+    f32x16 dq[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) dq[db] = (f32x16){};
+
+    auto tile = [&](auto par, int t) {
+        constexpr int PAR = decltype(par)::value;
+        wait_vm();
+        __syncthreads();
+        if (t + 1 < ntile) {
+            kplan.issue(kh, (t + 1) * C::BC, n_kv, kbuf(1 - PAR), w, lane);
+            vplan.issue(vh, (t + 1) * C::BC, n_kv, vbuf(1 - PAR), w, lane);
+        }
+        if (t >= wn) return;
+        f32x16 s[C::KB], dp[C::KB];
+        qk_tile<C>(s, kbuf(PAR), koff_k, qf);
+        qk_tile<C>(dp, vbuf(PAR), koff_v, gf);
+        // keys past n_kv, and (causal) keys after qi, have P = 0
+        const bool masked = (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
+        const int lim = C::CAUSAL ? min(n_kv, qi + 1) : n_kv;
+        v8 ds[C::KB][2];
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                v8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * k2 + e;
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
+                    if (masked) {
+                        const int key = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        pr = key < lim ? pr : 0.f;
+                    }
+                    x[e] = (T)(pr * (dp[kb][r] - dlt));
+                }
+                ds[kb][k2] = x;
+            }
+        pv_tile<C>(dq, kbuf(PAR), voff, ds);
+    };
+    for (int t = 0; t < ntile; t += 2) {
+        tile(std::integral_constant<int, 0>(), t);
+        if (t + 1 >= ntile) break;
+        tile(std::integral_constant<int, 1>(), t + 1);
+    }
+    if (qi < n_q) store_rows<C>(p.dq + ((int64_t)bh * n_q + qi) * C::RB, dq, p.scale, h);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (batch*head, block of 32*NW keys), streaming Q
+// and dO tiles of 64 query rows (both in the V-style layout: read by rows
+// and transposed) with the tiles' LSE_i log2(e) and D_i (LDS, after the
+// four tile buffers: [0, 256) LSE, [256, 512) D per buffer).
+template <class C>
+__global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams p) {
+    typedef typename C::T T;
+    typedef Mma16<T> M;
+    typedef typename M::v8 v8;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    auto qbuf = [&](int i) { return smem + i * C::TILE; };
+    auto gbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
+    auto sbuf = [&](int i) { return smem + 4 * C::TILE + i * 512; };
+
+    const int lane = lane_id();
+    const int w = wave_id();
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const int n_kblk = (p.n_kv + C::BR - 1) / C::BR;
+    const int bid = xcd_remap(blockIdx.x, p.n_bh * n_kblk);
+    const int bh = bid / n_kblk;
+    const int kb0 = bid - bh * n_kblk;
+    const int k0 = kb0 * C::BR;
+    const int wk0 = k0 + 32 * w;   // first key of this wave
+    const int kj = wk0 + l32;       // this lane's key
+    const int n_q = p.n_q, n_kv = p.n_kv;
+
+    const char *qh = p.q + (int64_t)bh * n_q * C::RB;
+    const char *gh = p.dout + (int64_t)bh * n_q * C::RB;
+    const float *lh = p.lse + (int64_t)bh * n_q;
+    const float *dh = p.delta + (int64_t)bh * n_q;
+
+    // query tiles [t0, ntile): causal rows before the block's first key see none of it
+    const int ntile = (n_q + C::BC - 1) / C::BC;
+    const int t0 = C::CAUSAL ? min(k0 / C::BC, ntile) : 0;
+    const int wt0 = C::CAUSAL ? min(wk0 / C::BC, ntile) : 0;  // this wave's first tile
+
+    const CopyPlan<C, true> plan(w, lane);
+    // LSE and D of tile t (wave 0: lanes 0-15 fetch LSE rows 4i..4i+3, lanes
+    // 16-31 the same rows of D); rows past n_q read as 0 through the buffer
+    // descriptors' bounds (their P is forced to 0 below)
+    auto issue_stats = [&](int t, char *dst) {
+        if (w == 0) {
+            const int rows = min(C::BC, n_q - t * C::BC);
+            if (lane < 16)
+                copy16_to_lds(make_rsrc(lh + t * C::BC, rows * 4), 16 * lane, dst);
+            else if (lane < 32)
+                copy16_to_lds(make_rsrc(dh + t * C::BC, rows * 4), 16 * (lane - 16), dst);
+        }
+    };
+    auto issue = [&](int t, int b) {
+        plan.issue(qh, t * C::BC, n_q, qbuf(b), w, lane);
+        plan.issue(gh, t * C::BC, n_q, gbuf(b), w, lane);
+        issue_stats(t, sbuf(b));
+    };
+    if (t0 < ntile) issue(t0, t0 & 1);
+
+    v8 kf[C::KS], vf[C::KS];
+    load_rows<C>(p.k + (int64_t)bh * n_kv * C::RB, kj, n_kv, kf, h);
+    load_rows<C>(p.v + (int64_t)bh * n_kv * C::RB, kj, n_kv, vf, h);
+    const float c = p.c;
+    const int koff = row_offset_v<C>(lane);
+    int voff[C::NVO];
+    tr_offsets<C>(lane, voff);
+
+    f32x16 dk[C::DB], dv[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+        dk[db] = (f32x16){};
+        dv[db] = (f32x16){};
+    }
+
+    for (int t = t0; t < ntile; ++t) {
+        const int cur = t & 1;
+        wait_vm();
+        __syncthreads();
+        if (t + 1 < ntile) issue(t + 1, 1 - cur);
+        if (t < wt0 || wk0 >= n_kv) continue;
+        const char *qt = qbuf(cur);
+        const char *gt = gbuf(cur);
+        // rows past n_q, and (causal) rows before this lane's key, have P = 0
+        const bool masked = (t + 1) * C::BC > n_q || (C::CAUSAL && t * C::BC < wk0 + 31);
+        const float *st = (const float *)sbuf(cur);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+            f32x16 s, dp;
+            qk_rows<C>(s, qt + 32 * kb * C::RB, koff, kf);
+            qk_rows<C>(dp, gt + 32 * kb * C::RB, koff, vf);
+            v8 pb[2], ds[2];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                // rows 32 kb + 16 k2 + 8 (e/4) + 4 h + e%4 of the tile
+                const f32x4 l_lo = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 4 * h);
+                const f32x4 l_hi = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 8 + 4 * h);
+                const f32x4 d_lo = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 4 * h);
+                const f32x4 d_hi = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 8 + 4 * h);
+                v8 xp, xs;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * k2 + e;
+                    const float l2 = (e < 4 ? l_lo[e & 3] : l_hi[e & 3]) * kLog2e;
+                    const float dl = e < 4 ? d_lo[e & 3] : d_hi[e & 3];
+                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+                    if (masked) {
+                        const int q = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        pr = (q < n_q && (!C::CAUSAL || kj <= q)) ? pr : 0.f;
+                    }
+                    xp[e] = (T)pr;
+                    xs[e] = (T)(pr * (dp[r] - dl));
+                }
+                pb[k2] = xp;
+                ds[k2] = xs;
+            }
+            pv_rows<C>(dv, gt + 32 * kb * C::RB, voff, pb);
+            pv_rows<C>(dk, qt + 32 * kb * C::RB, voff, ds);
+        }
+    }
+    if (kj < n_kv) {
+        const int64_t row = (int64_t)bh * n_kv + kj;
+        store_rows<C>(p.dk + row * C::RB, dk, p.scale, h);
+        store_rows<C>(p.dv + row * C::RB, dv, 1.f, h);
+    }
+}
+
+template <typename T, int D, int NWQ, int NWK, bool CAUSAL>
+int launch_bwd(const BwdParams &p, void *stream) {
+    typedef CfgB<T, D, NWQ, CAUSAL> CQ;
+    typedef CfgB<T, D, NWK, CAUSAL> CK;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t rows = (int64_t)p.n_bh * p.n_q;
+    if (rows > 0) {
+        constexpr int RPB = 256 / (D / 8);
+        hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                           st, p);
+        const int nq = (p.n_q + CQ::BR - 1) / CQ::BR;
+        hipLaunchKernelGGL(bwd_dq_kernel<CQ>, dim3(p.n_bh * nq), dim3(CQ::NT), 0, st, p);
+    }
+    const int nk = (p.n_kv + CK::BR - 1) / CK::BR;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<CK>, dim3(p.n_bh * nk), dim3(CK::NT), 0, st, p);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace
+
+#define FA_B16(T, DT, D, NWQ, NWK, CAUSAL)                                                  \
+    BwdVariant{DT, D, CAUSAL, "dq_w" #NWQ "_dkdv_w" #NWK, &launch_bwd<T, D, NWQ, NWK, CAUSAL>}
+
+// Host-side table of the compiled backward variants.
+const BwdVariant *bwd_variants(int *count) {
+    static const BwdVariant table[] = {
+        FA_B16(__bf16, FA_BF16, 64, 8, 4, 0),   FA_B16(__bf16, FA_BF16, 64, 8, 4, 1),
+        FA_B16(__bf16, FA_BF16, 128, 8, 4, 0),  FA_B16(__bf16, FA_BF16, 128, 8, 4, 1),
+        FA_B16(_Float16, FA_F16, 64, 8, 4, 0),  FA_B16(_Float16, FA_F16, 64, 8, 4, 1),
+        FA_B16(_Float16, FA_F16, 128, 8, 4, 0), FA_B16(_Float16, FA_F16, 128, 8, 4, 1),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace fa

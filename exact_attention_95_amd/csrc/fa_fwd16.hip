@@ -28,33 +28,18 @@
 // matrix products of the previous one.  A rescale of O decided by the
 // softmax of tile j+1 is applied at the start of iteration j+1, before P_{j+1}
 // is accumulated.  K and V tiles have two LDS buffers each and are filled by
-// direct global->LDS copies (global_load_lds_dwordx4): K two tiles ahead, V
+// direct copies to LDS (buffer_load_dwordx4 ... lds): K two tiles ahead, V
 // one tile ahead.  The causal variant stops at the diagonal tile (plate 07:
 // the mask is fused into the kernel) and masks only the tiles that straddle
 // it.
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_tile16.h"
 #include "../../include/fa.h"
 
 namespace fa {
 namespace {
-
-template <typename T> struct Mma16;
-template <> struct Mma16<__bf16> {
-    typedef bf16x8 v8;
-    typedef bf16x4 v4;
-    static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Mma16<_Float16> {
-    typedef f16x8 v8;
-    typedef f16x4 v4;
-    static __device__ __forceinline__ f32x16 mma(v8 a, v8 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-};
 
 // SPLIT: the workgroup covers one chunk of the key range (split-KV) and
 // writes a float32 partial output and LSE instead of O.
@@ -84,142 +69,6 @@ struct Cfg {
     static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
-
-// K rows: chunk c of row r is stored at chunk c ^ kswz(r).  With this XOR,
-// 16 lanes reading the same logical chunk of 16 consecutive rows touch 16
-// different 16-byte bank groups.
-template <class C> __device__ __forceinline__ int kswz(int r) { return (r / C::RPB) & C::KX; }
-// V rows: chunk c of row r is stored at chunk c ^ vswz(r); the transposed
-// reads cover 4 consecutive rows x 4 chunks per half-wave, which this XOR
-// spreads over 16 different bank groups.
-template <class C> __device__ __forceinline__ int vswz(int r) { return 4 * ((r / C::RPB) & C::VX); }
-
-// Per-lane part of the direct-to-LDS copies of one K (or V) tile: copy
-// instruction i of wave w moves chunks cb..cb+63 (cb = (i*NW + w)*64) of the
-// tile's LDS image; this lane's chunk is row r, physical chunk pc, so it
-// fetches logical chunk pc ^ swizzle(r) of row r.
-template <class C, bool IS_V>
-struct CopyPlan {
-    // Offsets are kept in registers only when there are few of them; wide
-    // heads (many copies per wave, many live accumulators) recompute them.
-    static constexpr bool KEEP = C::LDI <= 2;
-    unsigned off[KEEP ? C::LDI : 1];  // byte offset of the fetched chunk within a full tile
-    __device__ __forceinline__ static unsigned offset(int i, int w, int lane, int *row) {
-        const int chunk = (i * C::NW + w) * 64 + lane;
-        const int r = chunk / C::NC;
-        const int pc = chunk % C::NC;
-        const int sw = IS_V ? vswz<C>(r) : kswz<C>(r);
-        *row = r;
-        return (unsigned)(r * C::RB + 16 * (pc ^ sw));
-    }
-    __device__ __forceinline__ CopyPlan(int w, int lane) {
-        int r;
-        if (KEEP) {
-#pragma unroll
-            for (int i = 0; i < C::LDI; ++i) off[i] = offset(i, w, lane, &r);
-        }
-    }
-    // Issues the copies of rows [t0, t0 + BC) of one head into an LDS buffer,
-    // through a buffer resource that covers the head's rows [t0, n_kv).  Rows
-    // past n_kv (only in the last, ragged tile) are clamped to the last row:
-    // their scores are masked and their P entries are zero.
-    __device__ __forceinline__ void issue(const char *src, int t0, int n_kv, char *buf, int w,
-                                          int lane) const {
-        const int rows = min(C::BC, n_kv - t0);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + (int64_t)t0 * C::RB, rows * C::RB);
-        if (rows == C::BC) {
-#pragma unroll
-            for (int i = 0; i < C::LDI; ++i) {
-                int r;
-                const unsigned o = KEEP ? off[KEEP ? i : 0] : offset(i, w, lane, &r);
-                copy16_to_lds(rs, o, buf + (i * C::NW + w) * 1024);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::LDI; ++i) {
-                int r;
-                const unsigned o = offset(i, w, lane, &r);
-                const int gr = min(r, rows - 1);
-                copy16_to_lds(rs, o - (unsigned)((r - gr) * C::RB), buf + (i * C::NW + w) * 1024);
-            }
-        }
-    }
-};
-
-// v_permlane32_swap(a, b) returns ([a_lo, b_lo], [a_hi, b_hi]) (lo = lanes
-// 0-31, hi = lanes 32-63).  With a = b = x every lane thus receives the lower
-// half's x in the first result and the upper half's x in the second.  The
-// second operand is an opaque copy of x: the compiler would otherwise treat
-// the two results of a swap of identical operands as interchangeable.
-__device__ __forceinline__ void both_halves(float x, float &lo, float &hi) {
-    const unsigned u = __builtin_bit_cast(unsigned, x);
-    unsigned v;
-    asm("v_mov_b32 %0, %1" : "=v"(v) : "v"(u));
-    const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
-    lo = __builtin_bit_cast(float, (unsigned)r[0]);
-    hi = __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// Maximum / sum over the two half-waves (lanes l and l ^ 32), in every lane.
-__device__ __forceinline__ float max_halves(float x) {
-    float lo, hi;
-    both_halves(x, lo, hi);
-    return fmaxf(lo, hi);
-}
-
-__device__ __forceinline__ float sum_halves(float x) {
-    float lo, hi;
-    both_halves(x, lo, hi);
-    return lo + hi;
-}
-
-// S^T (32 keys x 32 queries per block) = K_tile Q^T.  The KB accumulation
-// chains are interleaved so that consecutive MFMAs are independent.  koff0
-// is this lane's LDS offset of k-step 0; k-step ks (< 8) is at koff0 ^ 32 ks
-// (the swizzled chunk index is (2 ks + h) ^ kswz, and 2 ks occupies bits the
-// row offset and the half-wave bit leave free), plus 256 per further 8 steps.
-// The offsets are recomputed per tile (the empty asm keeps the compiler from
-// hoisting them into registers that live across the whole loop).
-template <class C>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[C::KB], const char *Ks, int koff0,
-                                        const typename Mma16<typename C::T>::v8 (&qf)[C::KS]) {
-    typedef Mma16<typename C::T> M;
-    typedef typename M::v8 v8;
-    asm volatile("" : "+v"(koff0));
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = (f32x16){};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            const int ko = (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3);
-            const v8 a = *(const v8 *)(Ks + kb * 32 * C::RB + ko);
-            s[kb] = M::mma(a, qf[ks], s[kb]);
-        }
-}
-
-// O^T += V_tile^T P^T.  Register r of S^T block kb holds key
-// 32 kb + 8 (r/4) + 4 h + r%4, so the B operand of k-step (kb, k2) carries
-// keys 32 kb + 16 k2 + {0..3, 8..11} (+4 in the upper half-wave), and the
-// matching V^T operand is two transposed reads of 4 consecutive rows each.
-template <class C>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[C::DB], const char *Vs, const int (&voff)[C::NVO],
-                                        const typename Mma16<typename C::T>::v8 (&pb)[C::KB][2]) {
-    typedef Mma16<typename C::T> M;
-    typedef typename M::v8 v8;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + voff[db & 3] + 256 * (db >> 2);
-                const i16x4 lo = lds_read_tr16(base);
-                const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
-                const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[db] = M::mma(a, pb[kb][k2], o[db]);
-            }
-}
 
 // Masks the scores of one S^T tile for this lane's query row qi: keys past
 // n_kv, and (causal) keys after qi, become -inf.

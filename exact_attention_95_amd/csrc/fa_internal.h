@@ -51,4 +51,37 @@ const Variant *variants(int *count);
 // Merge of split-KV partials into O (output dtype) and LSE; 0 on success.
 int launch_merge(int dtype, int d, const KParams &p, void *stream);
 
+// Arguments of the backward kernels.  Byte pointers; each (batch, head)
+// slice is contiguous ([n_q, d] for Q, O, dO, dQ; [n_kv, d] for K, V, dK, dV).
+struct BwdParams {
+    const char *q;
+    const char *k;
+    const char *v;
+    const char *o;
+    const char *dout;
+    const float *lse;  // forward LSE, natural log
+    char *dq;
+    char *dk;
+    char *dv;
+    float *delta;      // workspace: D_i = sum_c dO_ic O_ic, [n_bh * n_q]
+    int n_bh;
+    int n_q;
+    int n_kv;
+    float c;           // scale * log2(e) (signed)
+    float scale;       // signed
+};
+
+// The three backward launches (D, dQ, dK/dV) for one (dtype, d, causal).
+typedef int (*bwd_launch_fn)(const BwdParams &p, void *stream);
+
+struct BwdVariant {
+    int dtype;
+    int d;
+    int causal;
+    const char *name;
+    bwd_launch_fn launch;
+};
+
+const BwdVariant *bwd_variants(int *count);
+
 }  // namespace fa

@@ -1,8 +1,9 @@
 """ctypes binding of the C ABI in include/fa.h (argument marshalling only).
 
 The functions ``fa_fwd``, ``fa_fwd_ex``, ``fa_validate``, ``fa_strerror``,
-``fa_num_variants`` and ``fa_variant_name`` mirror the C entry points of the
-same names.  ``fwd`` is the torch convenience form: it allocates O and LSE
+``fa_num_variants``, ``fa_variant_name``, ``fa_fwd_splitkv``,
+``fa_splitkv_workspace_bytes``, ``fa_bwd``, ``fa_bwd_validate`` and
+``fa_bwd_workspace_bytes`` mirror the C entry points of the same names.  ``fwd`` is the torch convenience form: it allocates O and LSE
 with torch on the inputs' device and calls ``fa_fwd_ex`` on torch's current
 stream.  All attention arithmetic runs in the HIP kernels; there is no CPU
 path, and the library must have been built (``exact_attention_95_amd.build``).
@@ -21,7 +22,8 @@ FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
  FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE) = range(12)
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
-            "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes")
+            "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_bwd",
+            "fa_bwd_validate", "fa_bwd_workspace_bytes")
 
 
 class FaFwdArgs(ctypes.Structure):
@@ -36,6 +38,20 @@ class FaFwdArgs(ctypes.Structure):
         ("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
         ("descale_v", ctypes.c_float),
         ("stream", ctypes.c_void_p), ("tile_override", ctypes.c_int),
+    ]
+
+
+class FaBwdArgs(ctypes.Structure):
+    """Mirror of ``fa_bwd_args``."""
+
+    _fields_ = [
+        ("Q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
+        ("O", ctypes.c_void_p), ("dO", ctypes.c_void_p), ("LSE", ctypes.c_void_p),
+        ("dQ", ctypes.c_void_p), ("dK", ctypes.c_void_p), ("dV", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N_q", ctypes.c_int64),
+        ("N_kv", ctypes.c_int64), ("d", ctypes.c_int64),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("stream", ctypes.c_void_p),
     ]
 
 
@@ -76,6 +92,12 @@ def load(path: str = LIB_PATH):
             lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int, vp, i64]
             lib.fa_splitkv_workspace_bytes.restype = i64
             lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int]
+            lib.fa_bwd.restype = ctypes.c_int
+            lib.fa_bwd.argtypes = [ctypes.POINTER(FaBwdArgs), vp, i64]
+            lib.fa_bwd_validate.restype = ctypes.c_int
+            lib.fa_bwd_validate.argtypes = [ctypes.POINTER(FaBwdArgs)]
+            lib.fa_bwd_workspace_bytes.restype = i64
+            lib.fa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FaBwdArgs)]
             _lib = lib
         return _lib
 
@@ -111,6 +133,18 @@ def fa_fwd_splitkv(args: FaFwdArgs, num_splits: int, workspace, workspace_bytes:
 
 def fa_splitkv_workspace_bytes(args: FaFwdArgs, num_splits: int) -> int:
     return load().fa_splitkv_workspace_bytes(ctypes.byref(args), num_splits)
+
+
+def fa_bwd(args: FaBwdArgs, workspace, workspace_bytes: int) -> int:
+    return load().fa_bwd(ctypes.byref(args), workspace, workspace_bytes)
+
+
+def fa_bwd_validate(args: FaBwdArgs) -> int:
+    return load().fa_bwd_validate(ctypes.byref(args))
+
+
+def fa_bwd_workspace_bytes(args: FaBwdArgs) -> int:
+    return load().fa_bwd_workspace_bytes(ctypes.byref(args))
 
 
 def _dtype_code(t) -> int:
@@ -217,3 +251,61 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
     if st != FA_OK:
         raise FaError(st)
     return out, lse
+
+
+def make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool,
+                  stream=None) -> FaBwdArgs:
+    """fa_bwd_args for torch tensors (shapes as in ``bwd``)."""
+    B, H, N_q, d = q.shape
+    a = FaBwdArgs()
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    a.Q, a.K, a.V, a.O, a.dO = ptr(q), ptr(k), ptr(v), ptr(o), ptr(do)
+    a.LSE = ptr(lse)
+    a.dQ, a.dK, a.dV = ptr(dq), ptr(dk), ptr(dv)
+    a.B, a.H, a.N_q, a.N_kv, a.d = B, H, N_q, k.shape[2], d
+    a.scale = scale
+    a.causal = int(bool(causal))
+    a.dtype = _dtype_code(q)
+    a.stream = stream
+    return a
+
+
+def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, stream=None,
+        workspace=None):
+    """Attention backward of torch device tensors; returns (dQ, dK, dV).
+
+    q, o, do: [B,H,N_q,d]; k, v: [B,H,N_kv,d] (bf16 or fp16, contiguous, one
+    gfx950 device); lse: [B,H,N_q] float32.  o and lse must be the forward's
+    outputs for these inputs, scale and causal.  The float32 workspace (D per
+    query row) is allocated with torch unless ``workspace`` (a uint8 device
+    tensor) is given.
+    """
+    import torch
+    for t in (q, k, v, o, lse, do):
+        if not t.is_cuda:
+            raise RuntimeError("fa.bwd needs GPU tensors; there is no CPU path")
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if len({q.dtype, k.dtype, v.dtype, o.dtype, do.dtype}) != 1:
+        raise TypeError("q, k, v, o, do must share a dtype")
+    if o.shape != q.shape or do.shape != q.shape or lse.shape != q.shape[:3] or k.shape != v.shape:
+        raise ValueError("shape mismatch")
+    B, H, N_q, d = q.shape
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    args = make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream)
+    need = fa_bwd_workspace_bytes(args)
+    if need < 0:
+        raise FaError(fa_bwd_validate(args))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_bwd(args, workspace.data_ptr(), workspace.numel())
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv

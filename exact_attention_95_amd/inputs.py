@@ -6,8 +6,8 @@ their inputs from here.
 
 Each (batch, head) slice of Q, K and V is drawn independently as i.i.d.
 N(0, 1) float32 from ``numpy.random.default_rng([seed_id, tensor_id, b, h])``
-(tensor_id 0 = Q, 1 = K, 2 = V), so any single head can be regenerated on
-its own.  Storage dtypes are produced by torch's round-to-nearest-even casts;
+(tensor_id 0 = Q, 1 = K, 2 = V; 4 = the upstream gradient dO of the backward
+pass), so any single head can be regenerated on its own.  Storage dtypes are produced by torch's round-to-nearest-even casts;
 E4M3 uses one scale per tensor that maps the absolute maximum to 448 and
 passes the reciprocal (as float32) on as the descale.
 """
@@ -57,6 +57,12 @@ class Workload:
         """Attention forward FLOPs: 4*B*H*N_q*N_kv*d, halved when causal."""
         f = 4.0 * self.B * self.H * self.n_q * self.n_kv * self.d
         return f / 2 if self.causal else f
+
+    @property
+    def bwd_flops(self) -> float:
+        """Attention backward FLOPs of its five matrix products (S recomputed,
+        dP, dV, dK, dQ): 10*B*H*N_q*N_kv*d, halved when causal."""
+        return 2.5 * self.flops
 
 
 # Workloads shaped like the ones the pages measure (see the design notes for
@@ -158,3 +164,9 @@ def random_problem(seed: int, B: int, H: int, n_q: int, n_kv: int, d: int,
     w = Workload("random_%d" % seed, 1000 + seed, B, H, n_q, n_kv, d, dtype, causal,
                  scale, boost_frac, boost)
     return w, make_inputs(w)
+
+
+def make_dout(w: Workload) -> torch.Tensor:
+    """Upstream gradient dO [B,H,N_q,d] for the backward pass: i.i.d. N(0,1)
+    per head (tensor_id 4), cast to w.dtype (bf16 or f16)."""
+    return torch.from_numpy(_tensor_f32(w, 4, w.n_q)).to(DTYPES[w.dtype])

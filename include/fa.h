@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) exact-attention forward library.
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library (forward,
+ * split-KV forward, backward).
  *
  * The operation is the attention of "FlashAttention算子优化" section 2 and
  * of "FlashAttention 与显存" plates 04, 07 and 08: for every batch b and head
@@ -144,6 +145,70 @@ int fa_fwd_splitkv(const fa_fwd_args *args, int num_splits, void *workspace,
  * fa_fwd_splitkv would reject.  Host-only, no HIP call.
  */
 int64_t fa_splitkv_workspace_bytes(const fa_fwd_args *args, int num_splits);
+
+/*
+ * Attention backward.  "FlashAttention 与显存" plate 09 keeps only O and the
+ * per-row statistic from the forward pass and recomputes S and P tile by tile
+ * when the gradients are needed; this entry point does that.  For every
+ * (batch, head), with S, P the forward's scores and probabilities (masked as
+ * in the forward) and dO the gradient of a loss with respect to O:
+ *     dV = P^T dO
+ *     dP = dO V^T,   D_i = sum_c dO_ic O_ic  (= sum_j P_ij dP_ij)
+ *     dS = P * (dP - D)     (elementwise; D_i broadcast along row i)
+ *     dQ = scale dS K,      dK = scale dS^T Q
+ * (the pages give no derivative formulas; these are the textbook gradients of
+ * softmax(scale Q K^T) V).  P is recomputed from Q, K and the forward's LSE
+ * as exp(scale q_i . k_j - LSE_i).
+ *
+ * Q, K, V, O, dO: device inputs; O and LSE must be the forward's outputs for
+ * these Q, K, V, scale and causal (fa_fwd / fa_fwd_ex), dO has O's shape and
+ * type.  dQ, dK, dV: device outputs with the type and layout of Q, K and V,
+ * written in full; they must not overlap each other, the inputs or the
+ * workspace (FA_ERR_ALIAS).  dtype: FA_BF16 or FA_F16 (else FA_ERR_DTYPE); d
+ * in {64, 128} (else FA_ERR_HEAD_DIM).  Other rules as for fa_fwd_ex (shapes,
+ * 16-byte alignment, finite scale, top-left causal mask).  B or H equal to 0
+ * is a no-op; N_q = 0 writes dK = dV = 0.
+ */
+typedef struct {
+    const void *Q;
+    const void *K;
+    const void *V;
+    const void *O;
+    const void *dO;
+    const float *LSE;
+    void *dQ;
+    void *dK;
+    void *dV;
+    int64_t B, H, N_q, N_kv, d;
+    float scale;
+    int causal;
+    int dtype;
+    void *stream;   /* hipStream_t; NULL = null stream */
+} fa_bwd_args;
+
+/*
+ * Validates args exactly as fa_bwd does (without the workspace checks),
+ * without any HIP call.  Returns FA_OK or the status fa_bwd would return.
+ */
+int fa_bwd_validate(const fa_bwd_args *args);
+
+/*
+ * Workspace bytes fa_bwd needs (float32 D, one value per query row, rounded
+ * up to 256 bytes); -1 for arguments fa_bwd_validate rejects.  Host-only.
+ */
+int64_t fa_bwd_workspace_bytes(const fa_bwd_args *args);
+
+/*
+ * Attention backward (see fa_bwd_args).  workspace: device memory owned by
+ * the caller, 256-byte aligned, at least fa_bwd_workspace_bytes(args) bytes,
+ * not overlapping any argument buffer (FA_ERR_WORKSPACE / FA_ERR_ALIAS
+ * otherwise); its contents are overwritten.  Three kernels run on
+ * args->stream, in order: D from dO and O, then dQ (one workgroup per query
+ * block), then dK and dV (one workgroup per key block).  No atomics: every
+ * output element is written by exactly one lane, so results are bitwise
+ * repeatable.
+ */
+int fa_bwd(const fa_bwd_args *args, void *workspace, int64_t workspace_bytes);
 
 /* Static, never-NULL description of a status code. */
 const char *fa_strerror(int status);

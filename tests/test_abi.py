@@ -164,3 +164,94 @@ def test_splitkv_workspace_bytes():
     assert fa.fa_splitkv_workspace_bytes(good_args(dtype=fa.FA_F32), 0) == -1
     assert fa.fa_splitkv_workspace_bytes(good_args(B=0), 0) == 0
     assert fa.fa_fwd_splitkv(good_args(B=0), 0, None, 0) == fa.FA_OK
+
+
+def test_bwd_args_struct_layout(tmp_path):
+    """The ctypes mirror matches the C compiler's layout of fa_bwd_args."""
+    fields = [f[0] for f in fa.FaBwdArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fa.h"\nint main(void){\n'
+                   + "".join('printf("%%zu\\n", offsetof(fa_bwd_args, %s));\n' % f for f in fields)
+                   + 'printf("%zu\\n", sizeof(fa_bwd_args)); return 0; }\n')
+    exe = tmp_path / "layout"
+    assert os.system("gcc -I%s -o %s %s" % (os.path.dirname(HEADER), exe, src)) == 0
+    got = [int(x) for x in os.popen(str(exe)).read().split()]
+    want = [getattr(fa.FaBwdArgs, f).offset for f in fields] + [ctypes.sizeof(fa.FaBwdArgs)]
+    assert got == want
+
+
+def good_bwd_args(**kw):
+    a = fa.FaBwdArgs()
+    # B*H*N*d*2 bytes = 2*3*100*64*2 = 76800 (Q-like), 2*3*90*64*2 = 69120 (K-like)
+    a.Q, a.K, a.V, a.O, a.dO, a.LSE = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+    a.dQ, a.dK, a.dV = 0x700000, 0x800000, 0x900000
+    a.B, a.H, a.N_q, a.N_kv, a.d = 2, 3, 100, 90, 64
+    a.scale = 0.125
+    a.causal = 0
+    a.dtype = fa.FA_BF16
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_bwd_validate_accepts_good_args():
+    for dt in (fa.FA_BF16, fa.FA_F16):
+        for d in (64, 128):
+            for causal in (0, 1):
+                assert fa.fa_bwd_validate(good_bwd_args(dtype=dt, d=d, causal=causal)) == fa.FA_OK
+    assert fa.fa_bwd_validate(good_bwd_args(scale=-3.0)) == fa.FA_OK
+    assert fa.fa_bwd_validate(good_bwd_args(scale=0.0)) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_DTYPE),
+    (dict(dtype=fa.FA_FP8_E4M3), fa.FA_ERR_DTYPE),
+    (dict(dtype=9), fa.FA_ERR_DTYPE),
+    (dict(d=256), fa.FA_ERR_HEAD_DIM),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM),
+    (dict(N_kv=0), fa.FA_ERR_SHAPE),
+    (dict(B=-1), fa.FA_ERR_SHAPE),
+    (dict(N_q=(1 << 30) + 1), fa.FA_ERR_SHAPE),
+    (dict(scale=math.nan), fa.FA_ERR_SCALE),
+    (dict(scale=math.inf), fa.FA_ERR_SCALE),
+    (dict(scale=3.0e38), fa.FA_ERR_SCALE),
+    (dict(dO=None), fa.FA_ERR_NULL),
+    (dict(LSE=None), fa.FA_ERR_NULL),
+    (dict(dQ=None), fa.FA_ERR_NULL),
+    (dict(dK=None), fa.FA_ERR_NULL),
+    (dict(O=0x400008), fa.FA_ERR_ALIGN),
+    (dict(dV=0x900004), fa.FA_ERR_ALIGN),
+    (dict(LSE=0x600002), fa.FA_ERR_ALIGN),
+    (dict(dQ=0x100000), fa.FA_ERR_ALIAS),                  # dQ on Q
+    (dict(dK=0x700000 + 64), fa.FA_ERR_ALIAS),             # dK inside dQ
+    (dict(dV=0x800000), fa.FA_ERR_ALIAS),                  # dV on dK
+    (dict(dQ=0x600000), fa.FA_ERR_ALIAS),                  # dQ over LSE
+])
+def test_bwd_validate_reports_each_status(kw, status):
+    assert fa.fa_bwd_validate(good_bwd_args(**kw)) == status
+
+
+def test_bwd_validate_null_args_and_empty_problems():
+    assert fa.load().fa_bwd_validate(None) == fa.FA_ERR_NULL
+    empty = good_bwd_args(B=0, Q=None, K=None, V=None, O=None, dO=None, LSE=None, dQ=None, dK=None, dV=None)
+    assert fa.fa_bwd_validate(empty) == fa.FA_OK
+    assert fa.fa_bwd_workspace_bytes(empty) == 0
+    assert fa.fa_bwd(empty, None, 0) == fa.FA_OK
+    # N_q = 0: only dK, dV (zeros) are written, so only K, V, dK, dV are needed
+    no_rows = good_bwd_args(N_q=0, Q=None, O=None, dO=None, LSE=None, dQ=None)
+    assert fa.fa_bwd_validate(no_rows) == fa.FA_OK
+    assert fa.fa_bwd_workspace_bytes(no_rows) == 0
+
+
+def test_bwd_workspace_bytes():
+    a = good_bwd_args()
+    assert fa.fa_bwd_workspace_bytes(a) == -(-2 * 3 * 100 * 4 // 256) * 256
+    assert fa.fa_bwd_workspace_bytes(good_bwd_args(d=256)) == -1
+
+
+def test_bwd_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(RuntimeError, match="GPU"):
+        fa.bwd(q, q, q, q, lse, q)

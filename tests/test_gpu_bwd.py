@@ -1,0 +1,149 @@
+"""Attention backward on the GPU against the fp64 oracle's gradients.
+
+The forward kernel produces O and LSE; the backward kernels take them with a
+seeded upstream gradient dO and return dQ, dK, dV, which must match the
+oracle's textbook gradients of the plain definition, computed from the same
+stored inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+from exact_attention_95_amd import fa
+from exact_attention_95_amd.inputs import WORKLOADS, make_dout, make_inputs, random_problem
+import oracle
+from parity import assert_grads_within, grad_errors, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+# (B, H, N_q, N_kv, d, dtype, causal)
+CASES = [
+    (1, 2, 200, 300, 64, "bf16", False),
+    (1, 2, 333, 333, 128, "bf16", True),
+    (2, 1, 128, 128, 128, "f16", False),
+    (1, 1, 70, 500, 64, "f16", True),
+    (1, 2, 520, 260, 128, "bf16", True),
+    (1, 1, 1, 64, 128, "bf16", False),
+    (1, 1, 40, 1, 64, "bf16", False),
+    (1, 1, 300, 37, 128, "f16", True),
+    (1, 1, 1000, 1000, 128, "bf16", False),
+]
+
+
+def run_bwd(w, x, dout):
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    do = dout.cuda()
+    o, lse = fa.fwd(q, k, v, scale=w.sm_scale, causal=w.causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, scale=w.sm_scale, causal=w.causal)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def to64(t):
+    return t.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)), ids=["x".join(str(v) for v in c) for c in CASES])
+def test_bwd_matches_oracle(idx):
+    B, H, nq, nkv, d, dt, causal = CASES[idx]
+    w, x = random_problem(400 + idx, B, H, nq, nkv, d, dt, causal)
+    dout = make_dout(w)
+    say("case", CASES[idx])
+    dq, dk, dv = run_bwd(w, x, dout)
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], dout, w.sm_scale, causal)
+    errs = {"dQ": grad_errors(to64(dq), rq), "dK": grad_errors(to64(dk), rk), "dV": grad_errors(to64(dv), rv)}
+    say(errs)
+    assert_grads_within(errs, str(CASES[idx]))
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
+def test_bwd_scales(scale):
+    w, x = random_problem(420, 1, 2, 150, 190, 64, "bf16", True, scale=scale)
+    dout = make_dout(w)
+    dq, dk, dv = run_bwd(w, x, dout)
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], dout, w.sm_scale, True)
+    errs = {"dQ": grad_errors(to64(dq), rq), "dK": grad_errors(to64(dk), rk), "dV": grad_errors(to64(dv), rv)}
+    say(scale, errs)
+    if scale == 0.0:
+        assert torch.count_nonzero(dq) == 0 and torch.count_nonzero(dk) == 0
+        assert_grads_within({"dV": errs["dV"]}, "scale 0")
+    else:
+        assert_grads_within(errs, "scale %g" % scale)
+
+
+def test_bwd_repeatable_and_key_gradients_sum_to_zero():
+    w, x = random_problem(421, 1, 2, 256, 320, 128, "bf16", False)
+    dout = make_dout(w)
+    a = run_bwd(w, x, dout)
+    b = run_bwd(w, x, dout)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    # softmax is unchanged by one shift of all keys: sum_j dK_j = 0 up to rounding
+    dk = a[1].double()
+    col = dk.sum(dim=2).abs().max().item()
+    assert col <= 1e-2 * dk.abs().sum(dim=2).max().item()
+
+
+def test_bwd_no_query_rows_gives_zero_key_gradients():
+    k = torch.randn(1, 2, 100, 64, device="cuda").to(torch.bfloat16)
+    v = torch.randn(1, 2, 100, 64, device="cuda").to(torch.bfloat16)
+    q = torch.empty(1, 2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(1, 2, 0, device="cuda")
+    dq, dk, dv = fa.bwd(q, k, v, q, lse, q)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and torch.count_nonzero(dk) == 0 and torch.count_nonzero(dv) == 0
+
+
+def test_bwd_errors():
+    w, x = random_problem(422, 1, 1, 64, 64, 64, "bf16", False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, scale=w.sm_scale)
+    do = make_dout(w).cuda()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    args = fa.make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, w.sm_scale, False)
+    need = fa.fa_bwd_workspace_bytes(args)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    assert fa.fa_bwd(args, ws.data_ptr(), need - 1) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd(args, ws.data_ptr() + 16, need) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd(args, None, need) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd(args, q.data_ptr(), need) in (fa.FA_ERR_ALIAS, fa.FA_ERR_WORKSPACE)
+    assert fa.fa_bwd(args, ws.data_ptr(), need) == fa.FA_OK
+    torch.cuda.synchronize()
+    bad = fa.make_bwd_args(q, k, v, o, lse, do, q, dk, dv, w.sm_scale, False)  # dQ on Q
+    assert fa.fa_bwd(bad, ws.data_ptr(), need) == fa.FA_ERR_ALIAS
+    with pytest.raises(fa.FaError):
+        fa.bwd(q.float(), k.float(), v.float(), o.float(), lse, do.float())
+
+
+@pytest.mark.parametrize("name", ["headline_bf16_n8192_d128", "headline_bf16_causal_n8192_d128",
+                                  "gpt2_medium_bf16_n1024_d64"])
+def test_bwd_full_size_sampled(name):
+    """Full-size backward in the launch configuration the benchmark times;
+    the oracle checks dQ on sampled rows and dK, dV on sampled keys of two
+    heads (every boosted row of those heads among them)."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    dout = make_dout(w)
+    dq, dk, dv = run_bwd(w, x, dout)
+    rng = np.random.default_rng([w.seed_id, 77])
+    heads = rng.choice(w.B * w.H, size=2, replace=False)
+    rows, keys = [], []
+    for bh in heads:
+        base_q, base_k = bh * w.n_q, bh * w.n_kv
+        rows.append(base_q + rng.integers(0, w.n_q, 96))
+        rows.append(base_q + np.array([0, 1, 63, 64, 127, 128, 255, 256, w.n_q - 1]))
+        b = x["boost_rows"]
+        rows.append(b[(b >= base_q) & (b < base_q + w.n_q)])
+        keys.append(base_k + rng.integers(0, w.n_kv, 96))
+        keys.append(base_k + np.array([0, 1, 31, 32, 127, 128, w.n_kv - 1]))
+    rows = np.unique(np.concatenate(rows)).astype(np.int64)
+    keys = np.unique(np.concatenate(keys)).astype(np.int64)
+    sel = lambda t, idx: to64(t.reshape(-1, w.d)[torch.from_numpy(idx).cuda()])
+    gq, gk, gv = sel(dq, rows), sel(dk, keys), sel(dv, keys)
+    del dq, dk, dv
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], dout, w.sm_scale, w.causal, rows=rows, keys=keys)
+    errs = {"dQ": grad_errors(gq, rq), "dK": grad_errors(gk, rk), "dV": grad_errors(gv, rv)}
+    say(name, rows.size, keys.size, errs)
+    assert_grads_within(errs, name)
