@@ -28,11 +28,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("attention fwd TFLOP/s (4·B·H·N²·d) and % of MFMA peak, "
           "bf16 N=8K d=128")
+BWD_METRIC = "attention bwd TFLOP/s (10·B·H·N²·d: S, dP, dV, dK, dQ) and % of MFMA peak"
 DEFAULT_WORKLOAD = "headline_bf16_n8192_d128"
 # MI355X dense peaks, TFLOP/s: 256 CUs x 2.4 GHz x flop/clk/CU of the matrix cores
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "fp8_e4m3": 5033.2, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 ELEM_BYTES = {"bf16": 2, "f16": 2, "fp8_e4m3": 1, "f32": 4}
+
+
+def algorithmic_bytes_bwd(w) -> float:
+    """Backward: Q, K, V, O, dO and LSE read once; dQ, dK, dV written once."""
+    e = ELEM_BYTES[w.dtype]
+    return float(w.B * w.H * ((4 * w.n_q + 4 * w.n_kv) * w.d * e + 8 * w.n_q))
 
 
 def algorithmic_bytes(w) -> float:
@@ -48,26 +55,30 @@ KERNEL_SOURCE = {"f32": "fa_fwd32.hip", "f16": "fa_fwd16.hip", "bf16": "fa_fwd16
                  "fp8_e4m3": "fa_fwd8.hip"}
 
 
-def kernel_source_digest(dtype: str) -> str:
+def kernel_source_digest(dtype: str, bwd: bool = False) -> str:
     """Hash of the sources that make the workload's kernel (its .hip file, the
-    shared device and launch code), to tell whether stored counters still apply."""
+    shared device, tile and launch code), to tell whether stored counters
+    still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_95_amd", "csrc")
-    for name in sorted(["fa_device.h", "fa_internal.h", "fa_api.cpp", KERNEL_SOURCE[dtype]]):
+    names = ["fa_device.h", "fa_internal.h", "fa_api.cpp", "fa_bwd16.hip" if bwd else KERNEL_SOURCE[dtype]]
+    if bwd or dtype in ("f16", "bf16"):
+        names.append("fa_tile16.h")
+    for name in sorted(names):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, dtype: str):
+def stored_traffic(workload: str, dtype: str, bwd: bool = False):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
-    path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % workload)
+    path = os.path.join(TRAFFIC_DIR, "traffic_%s%s.json" % (workload, "_bwd" if bwd else ""))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_digest") != kernel_source_digest(dtype):
+    if rec.get("kernel_source_digest") != kernel_source_digest(dtype, bwd):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -114,7 +125,38 @@ def cpu_baseline(w, x, target_s: float = 15.0) -> dict:
     }
 
 
-def summarize_counters(workload: str, fetch_csv: str, write_csv: str) -> dict:
+def cpu_baseline_bwd(w, x, dout, target_s: float = 15.0) -> dict:
+    """The fp64 oracle's gradients (as they stand) on whole heads of the same
+    workload: one head, then more until a run takes about target_s seconds.
+    Counted with the metric's algorithmic FLOPs (10 N_q N_kv d per head,
+    halved when causal)."""
+    import oracle
+    total = w.B * w.H
+    n = 1
+    while True:
+        heads = list(range(n))
+        q = np.stack([x["q"].reshape(total, w.n_q, w.d)[i].double().numpy() for i in heads])[:, None]
+        k = np.stack([x["k"].reshape(total, w.n_kv, w.d)[i].double().numpy() for i in heads])[:, None]
+        v = np.stack([x["v"].reshape(total, w.n_kv, w.d)[i].double().numpy() for i in heads])[:, None]
+        g = np.stack([dout.reshape(total, w.n_q, w.d)[i].double().numpy() for i in heads])[:, None]
+        t0 = time.perf_counter()
+        oracle.backward(q, k, v, g, w.sm_scale, w.causal)
+        dt = time.perf_counter() - t0
+        if dt >= 0.6 * target_s or n == total:
+            break
+        n = int(min(total, max(n + 1, n * target_s / max(dt, 1e-3))))
+    f = w.bwd_flops / total * n
+    return {
+        "value": round(f / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d heads of workload %s (whole heads); fp64 oracle gradients, %.1f s, "
+                  "%.4g FLOP counted as 10*N_q*N_kv*d per head" % (n, total, w.name, dt, f),
+    }
+
+
+def summarize_counters(workload: str, fetch_csv: str, write_csv: str, bwd: bool = False) -> dict:
     """HBM bytes per launch of the attention kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
     counter reads for a plain 1 GiB device copy (hipMemcpy's copy kernel) run
@@ -132,19 +174,22 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str) -> dict:
     def factor_and_value(path, counter):
         rows = per_kernel(path, counter)
         copy = [v for k, vals in rows.items() if "copyBuffer" in k for v in vals]
-        fa_vals = [v for k, vals in rows.items() if "fwd" in k and "fa" in k for v in vals]
-        if not copy or not fa_vals:
+        # per launch: the forward kernel, or the sum of the backward's three
+        # kernels (each averaged over its dispatches)
+        key = "bwd_" if bwd else "fwd"
+        groups = [vals for k, vals in rows.items() if key in k and "fa" in k]
+        if not copy or not groups:
             raise RuntimeError("missing copy or attention dispatches in %s" % path)
         copy_kib = sorted(copy)[len(copy) // 2]
         factor = (1 << 30) / (copy_kib * 1024.0)
-        value = sum(fa_vals) / len(fa_vals) * 1024.0
+        value = sum(sum(v) / len(v) for v in groups) * 1024.0
         return factor, value
 
     ff, fetch = factor_and_value(fetch_csv, "FETCH_SIZE")
     wf, write = factor_and_value(write_csv, "WRITE_SIZE")
     rec = {
-        "workload": workload,
-        "kernel_source_digest": kernel_source_digest(WORKLOADS[workload].dtype),
+        "workload": workload + ("_bwd" if bwd else ""),
+        "kernel_source_digest": kernel_source_digest(WORKLOADS[workload].dtype, bwd),
         "fetch_bytes_raw": fetch, "fetch_factor": ff,
         "write_bytes_raw": write, "write_factor": wf,
         "hbm_bytes_per_launch": round(fetch * ff + write * wf),
@@ -190,6 +235,8 @@ def main(argv=None) -> int:
     ap.add_argument("--splitkv", type=int, default=None,
                     help="use the split-KV entry point with this many chunks (0: library "
                          "choice, -1: off); default: on for workloads with at most 16 query rows")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (fa_bwd: dQ, dK, dV) instead of the forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -202,8 +249,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.summarize_counters:
-        rec = summarize_counters(args.workload, *args.summarize_counters)
-        path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % args.workload)
+        rec = summarize_counters(args.workload, *args.summarize_counters, bwd=args.bwd)
+        path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % rec["workload"])
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
@@ -216,7 +263,7 @@ def main(argv=None) -> int:
 
     import torch
     from exact_attention_95_amd import fa
-    from exact_attention_95_amd.inputs import WORKLOADS, make_inputs
+    from exact_attention_95_amd.inputs import WORKLOADS, make_dout, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -258,6 +305,27 @@ def main(argv=None) -> int:
             s = fa.fa_fwd_ex(fargs)
             if s != fa.FA_OK:
                 raise fa.FaError(s)
+    check = o
+    if args.bwd:
+        if w.dtype not in ("bf16", "f16") or w.d not in (64, 128):
+            print("the backward covers bf16/fp16 with d in {64, 128}", file=sys.stderr)
+            return 2
+        # the forward's O and LSE, then the timed step is one fa_bwd call
+        step()
+        do = make_dout(w).to(dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bargs = fa.make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, w.sm_scale, w.causal,
+                                 stream.cuda_stream)
+        bneed = fa.fa_bwd_workspace_bytes(bargs)
+        if bneed < 0:
+            raise fa.FaError(fa.fa_bwd_validate(bargs))
+        bws = torch.empty(max(bneed, 256), dtype=torch.uint8, device=dev)
+        check = dk
+
+        def step():
+            s = fa.fa_bwd(bargs, bws.data_ptr(), bws.numel())
+            if s != fa.FA_OK:
+                raise fa.FaError(s)
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
@@ -273,7 +341,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    if not bool(torch.isfinite(o.float()).all()):
+    if not bool(torch.isfinite(check.float()).all()):
         print("non-finite output", file=sys.stderr)
         return 1
 
@@ -286,9 +354,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    flops = w.flops
+    flops = w.bwd_flops if args.bwd else w.flops
     value = flops * args.steps / wall / 1e12
-    nbytes = algorithmic_bytes(w)
+    nbytes = algorithmic_bytes_bwd(w) if args.bwd else algorithmic_bytes(w)
     # the bound of the dominant kernel: HBM when the arithmetic intensity is
     # below the dtype's ridge point, else the matrix cores
     hbm_bound = flops / nbytes < PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -297,7 +365,7 @@ def main(argv=None) -> int:
     else:
         achieved, peak, unit = flops / (kernel_ms * 1e-3) / 1e12, PEAK_TFLOPS[w.dtype], "TFLOP/s"
     rec = {
-        "metric": METRIC,
+        "metric": BWD_METRIC if args.bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -311,16 +379,18 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.n_q, "N_kv": w.n_kv,
                    "d": w.d, "causal": w.causal, "dtype": w.dtype,
-                   "variant": ("split_kv(%s)" % ("auto" if splitkv == 0 else splitkv)
+                   "variant": ("backward" if args.bwd else
+                               "split_kv(%s)" % ("auto" if splitkv == 0 else splitkv)
                                if splitkv is not None else
                                fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1)),
                    "flops_per_step": flops, "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": stored_traffic(w.name, w.dtype), "kernel_ms": round(kernel_ms, 4)},
+                     "traffic": stored_traffic(w.name, w.dtype, args.bwd),
+                     "kernel_ms": round(kernel_ms, 4)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, x)
+        rec["cpu_baseline"] = (cpu_baseline_bwd(w, x, do.cpu()) if args.bwd else cpu_baseline(w, x))
     print(json.dumps(rec), flush=True)
     return 0
 
