@@ -43,8 +43,10 @@ struct CfgB {
     static constexpr int KS = D / 16, KB = BC / 32, DB = D / 32, LDI = TILE / (1024 * NW);
     static constexpr int NVO = DB < 4 ? DB : 4;
     static constexpr int LDS = 4 * TILE + 2 * 512;  // two streams x two buffers, + LSE/D tiles
-    // wave count per SIMD the register budget must allow
-    static constexpr int MIN_WAVES = 1;
+    // waves per SIMD the register budget must allow: at d = 64 the dK/dV
+    // kernel fits two (two workgroups of 4 waves per CU); at d = 128 its
+    // accumulators alone take 128 registers and it runs one
+    static constexpr int MIN_WAVES = D <= 64 ? 2 : 1;
     static_assert(TILE % (1024 * NW) == 0, "tile must split into whole wave copies");
 };
 
@@ -330,50 +332,128 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         dv[db] = (f32x16){};
     }
 
-    for (int t = t0; t < ntile; ++t) {
+    // P and dS of one 32-row block kb of the tile (VALU), from its S and dP
+    auto elementwise = [&](auto mk, int t, const float *st, int kb, const f32x16 &s, const f32x16 &dp,
+                           v8 (&pb)[2], v8 (&ds)[2]) {
+        constexpr bool MK = decltype(mk)::value;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            // rows 32 kb + 16 k2 + 8 (e/4) + 4 h + e%4 of the tile
+            const f32x4 l_lo = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 4 * h);
+            const f32x4 l_hi = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 8 + 4 * h);
+            const f32x4 d_lo = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 4 * h);
+            const f32x4 d_hi = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 8 + 4 * h);
+            v8 xp, xs;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = 8 * k2 + e;
+                const float l2 = (e < 4 ? l_lo[e & 3] : l_hi[e & 3]) * kLog2e;
+                const float dl = e < 4 ? d_lo[e & 3] : d_hi[e & 3];
+                float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
+                if (MK) {
+                    // rows past n_q, and (causal) rows before this lane's key, have P = 0
+                    const int q = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    pr = (q < n_q && (!C::CAUSAL || kj <= q)) ? pr : 0.f;
+                }
+                xp[e] = (T)pr;
+                xs[e] = (T)(pr * (dp[r] - dl));
+            }
+            pb[k2] = xp;
+            ds[k2] = xs;
+        }
+    };
+    // One tile, software-pipelined over its two 32-row blocks in four
+    // scheduling segments: S, dP of block 0; S, dP of block 1 under the VALU
+    // of block 0; dV, dK of block 0 under the VALU of block 1; dV, dK of
+    // block 1.
+    auto body = [&](auto mk, int t) {
         const int cur = t & 1;
-        wait_vm();
-        __syncthreads();
-        if (t + 1 < ntile) issue(t + 1, 1 - cur);
-        if (t < wt0 || wk0 >= n_kv) continue;
         const char *qt = qbuf(cur);
         const char *gt = gbuf(cur);
-        // rows past n_q, and (causal) rows before this lane's key, have P = 0
-        const bool masked = (t + 1) * C::BC > n_q || (C::CAUSAL && t * C::BC < wk0 + 31);
         const float *st = (const float *)sbuf(cur);
+        f32x16 s[2], dp[2];
+        v8 pb[2][2], ds[2][2];
+        constexpr int NQK = 2 * C::KS, NPV = 4 * C::DB;  // MFMAs of two products, per block
+        // segment A: S, dP of block 0
+        qk_rows<C>(s[0], qt, koff, kf);
+        qk_rows<C>(dp[0], gt, koff, vf);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-            f32x16 s, dp;
-            qk_rows<C>(s, qt + 32 * kb * C::RB, koff, kf);
-            qk_rows<C>(dp, gt + 32 * kb * C::RB, koff, vf);
-            v8 pb[2], ds[2];
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                // rows 32 kb + 16 k2 + 8 (e/4) + 4 h + e%4 of the tile
-                const f32x4 l_lo = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 4 * h);
-                const f32x4 l_hi = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 8 + 4 * h);
-                const f32x4 d_lo = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 4 * h);
-                const f32x4 d_hi = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 8 + 4 * h);
-                v8 xp, xs;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * k2 + e;
-                    const float l2 = (e < 4 ? l_lo[e & 3] : l_hi[e & 3]) * kLog2e;
-                    const float dl = e < 4 ? d_lo[e & 3] : d_hi[e & 3];
-                    float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
-                    if (masked) {
-                        const int q = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        pr = (q < n_q && (!C::CAUSAL || kj <= q)) ? pr : 0.f;
-                    }
-                    xp[e] = (T)pr;
-                    xs[e] = (T)(pr * (dp[r] - dl));
-                }
-                pb[k2] = xp;
-                ds[k2] = xs;
-            }
-            pv_rows<C>(dv, gt + 32 * kb * C::RB, voff, pb);
-            pv_rows<C>(dk, qt + 32 * kb * C::RB, voff, ds);
+        for (int i = 0; i < NQK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // segment B: S, dP of block 1 under the VALU of block 0
+        qk_rows<C>(s[1], qt + 32 * C::RB, koff, kf);
+        qk_rows<C>(dp[1], gt + 32 * C::RB, koff, vf);
+        elementwise(mk, t, st, 0, s[0], dp[0], pb[0], ds[0]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // segment C: dV, dK of block 0 under the VALU of block 1
+        pv_rows<C>(dv, gt, voff, pb[0]);
+        pv_rows<C>(dk, qt, voff, ds[0]);
+        elementwise(mk, t, st, 1, s[1], dp[1], pb[1], ds[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // segment D: dV, dK of block 1
+        pv_rows<C>(dv, gt + 32 * C::RB, voff, pb[1]);
+        pv_rows<C>(dk, qt + 32 * C::RB, voff, ds[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+        }
+    };
+    auto sync_issue = [&](int t) {
+        wait_vm();
+        __syncthreads();
+        if (t + 1 < ntile) issue(t + 1, 1 - (t & 1));
+    };
+    static_assert(C::KB == 2, "two 32-row blocks per tile");
+    // Tiles in order, each loop with one body (a branch between a masked and
+    // an unmasked body inside one loop makes the compiler move the dK, dV
+    // accumulators between AGPRs and VGPRs on every tile):
+    //   [t0, wt0)        rows before this wave's keys: barriers and copies only
+    //   [wt0, tm)        causal: tiles below some key of this wave, masked
+    //   [tm, tf)         full tiles, unmasked
+    //   [tf, ntile)      the ragged last tile, masked
+    const int tm = C::CAUSAL ? max(wt0, min(ntile, (wk0 + 31) / C::BC + 1)) : wt0;
+    const int tf = max(tm, min(ntile, n_q / C::BC));
+    auto pin = [&]() {
+        // keeps the accumulators in AGPRs across iterations
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+    };
+    int t = t0;
+    for (; t < wt0; ++t) sync_issue(t);
+    for (; t < tm; ++t) {
+        sync_issue(t);
+        body(std::integral_constant<bool, true>(), t);
+        pin();
+    }
+    for (; t < tf; ++t) {
+        sync_issue(t);
+        body(std::integral_constant<bool, false>(), t);
+        pin();
+    }
+    for (; t < ntile; ++t) {
+        sync_issue(t);
+        body(std::integral_constant<bool, true>(), t);
+        pin();
     }
     if (kj < n_kv) {
         const int64_t row = (int64_t)bh * n_kv + kj;
