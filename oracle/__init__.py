@@ -87,6 +87,23 @@ def _declare(lib):
     lib.fa_oracle_backward.argtypes = [
         _dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
         ctypes.c_int, _i64p, ctypes.c_int64, _i64p, ctypes.c_int64, _dp, _dp, _dp]
+    _u32p = ctypes.POINTER(ctypes.c_uint32)
+    _u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.fa_oracle_philox4x32_10.restype = None
+    lib.fa_oracle_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
+    lib.fa_oracle_dropout_p8.restype = ctypes.c_int
+    lib.fa_oracle_dropout_p8.argtypes = [ctypes.c_double]
+    lib.fa_oracle_dropout_mask.restype = ctypes.c_int
+    lib.fa_oracle_dropout_mask.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int, _u8p]
+    lib.fa_oracle_attention_dropout.restype = ctypes.c_int
+    lib.fa_oracle_attention_dropout.argtypes = [
+        _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+        _u8p, ctypes.c_double, _dp, _dp]
+    lib.fa_oracle_backward_dropout.restype = ctypes.c_int
+    lib.fa_oracle_backward_dropout.argtypes = [
+        _dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+        ctypes.c_int, _u8p, ctypes.c_double, _dp, _dp, _dp]
     lib.fa_oracle_merge.restype = ctypes.c_int
     lib.fa_oracle_merge.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
     lib.fa_oracle_num_threads.restype = ctypes.c_int
@@ -282,6 +299,88 @@ def backward(q, k, v, dout, scale: float, causal: bool = False, rows=None, keys=
     dq = dq.reshape(B, H, n_q, d)
     dk = dk.reshape(B, H, n_kv, d)
     dv = dv.reshape(B, H, n_kv, d)
+    if q.ndim == 2:
+        return dq[0, 0], dk[0, 0], dv[0, 0]
+    return dq, dk, dv
+
+
+def philox4x32_10(ctr, key, lib=None):
+    """Philox4x32-10 of a 4-word counter and 2-word key; returns 4 words."""
+    lib = lib or load()
+    c = (ctypes.c_uint32 * 4)(*[int(x) & 0xFFFFFFFF for x in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib.fa_oracle_philox4x32_10(c, k, o)
+    return [int(x) for x in o]
+
+
+def dropout_p8(p: float, lib=None) -> int:
+    """The dropout probability quantised to p8 / 256."""
+    return int((lib or load()).fa_oracle_dropout_p8(float(p)))
+
+
+def dropout_rescale(p8: int) -> float:
+    return 256.0 / (256.0 - p8)
+
+
+def dropout_mask(seed: int, offset: int, bh: int, n_q: int, n_kv: int, p8: int, lib=None) -> np.ndarray:
+    """[n_q, n_kv] uint8 keep mask (1 = kept) of slice bh."""
+    lib = lib or load()
+    m = np.empty((n_q, n_kv), dtype=np.uint8)
+    st = lib.fa_oracle_dropout_mask(int(seed) & (2**64 - 1), int(offset) & (2**64 - 1), int(bh), n_q, n_kv,
+                                    int(p8), m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    if st:
+        raise RuntimeError("fa_oracle_dropout_mask failed: %d" % st)
+    return m
+
+
+def attention_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int,
+                      lib=None):
+    """Attention with dropout in fp64 ([B,H,N,d] or [N,d]); returns (O, LSE)."""
+    lib = lib or load()
+    q4, k4, v4 = (_heads(t) for t in (q, k, v))
+    B, H, n_q, d = q4.shape
+    n_kv = k4.shape[2]
+    p8 = dropout_p8(p, lib)
+    o = np.empty((B, H, n_q, d))
+    lse = np.empty((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            keep = dropout_mask(seed, offset, b * H + h, n_q, n_kv, p8, lib)
+            qh, kh, vh = _as_f64(q4[b, h]), _as_f64(k4[b, h]), _as_f64(v4[b, h])
+            oh, lh = np.empty((n_q, d)), np.empty(n_q)
+            st = lib.fa_oracle_attention_dropout(
+                _ptr(qh), _ptr(kh), _ptr(vh), n_q, n_kv, d, float(scale), int(bool(causal)),
+                keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), dropout_rescale(p8), _ptr(oh), _ptr(lh))
+            if st:
+                raise RuntimeError("fa_oracle_attention_dropout failed: %d" % st)
+            o[b, h], lse[b, h] = oh, lh
+    if q.ndim == 2:
+        return o[0, 0], lse[0, 0]
+    return o, lse
+
+
+def backward_dropout(q, k, v, dout, scale: float, causal: bool, p: float, seed: int, offset: int,
+                     lib=None):
+    """Gradients of attention_dropout in fp64; returns (dQ, dK, dV)."""
+    lib = lib or load()
+    q4, k4, v4, g4 = (_heads(t) for t in (q, k, v, dout))
+    B, H, n_q, d = q4.shape
+    n_kv = k4.shape[2]
+    p8 = dropout_p8(p, lib)
+    dq, dk, dv = np.empty((B, H, n_q, d)), np.empty((B, H, n_kv, d)), np.empty((B, H, n_kv, d))
+    for b in range(B):
+        for h in range(H):
+            keep = dropout_mask(seed, offset, b * H + h, n_q, n_kv, p8, lib)
+            qh, kh, vh, gh = (_as_f64(t[b, h]) for t in (q4, k4, v4, g4))
+            a, bk, c = np.empty((n_q, d)), np.empty((n_kv, d)), np.empty((n_kv, d))
+            st = lib.fa_oracle_backward_dropout(
+                _ptr(qh), _ptr(kh), _ptr(vh), _ptr(gh), n_q, n_kv, d, float(scale), int(bool(causal)),
+                keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), dropout_rescale(p8),
+                _ptr(a), _ptr(bk), _ptr(c))
+            if st:
+                raise RuntimeError("fa_oracle_backward_dropout failed: %d" % st)
+            dq[b, h], dk[b, h], dv[b, h] = a, bk, c
     if q.ndim == 2:
         return dq[0, 0], dk[0, 0], dv[0, 0]
     return dq, dk, dv

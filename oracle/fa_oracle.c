@@ -447,6 +447,181 @@ int fa_oracle_backward(const double *q, const double *k, const double *v, const 
 }
 
 /*
+ * Dropout (a training-time feature "FlashAttention 与显存" plates 07 and 09
+ * name for the fused kernel, with the random state replayed in the backward
+ * pass).  The pages specify no generator; this one is Philox4x32-10
+ * (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+ * 1, 2, 3", SC 2011), written from that paper's definition: 10 rounds of
+ *   (hi0, lo0) = M0 * c0,  (hi1, lo1) = M1 * c2   (32x32 -> 64-bit products)
+ *   c = (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
+ * with M0 = 0xD2511F53, M1 = 0xCD9E8D57, and the key bumped by the Weyl
+ * constants (0x9E3779B9, 0xBB67AE85) after every round.
+ */
+void fa_oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/*
+ * Dropout threshold: p is quantised to p8 / 256, p8 = floor(p * 256 + 1/2)
+ * clamped to [0, 255]; 0 means no dropout.
+ */
+int fa_oracle_dropout_p8(double p)
+{
+    double x = floor(p * 256.0 + 0.5);
+    if (x < 0.0) x = 0.0;
+    if (x > 255.0) x = 255.0;
+    return (int)x;
+}
+
+/*
+ * Keep mask of one (batch, head) slice, bh = b * H + h: element (i, j) is
+ * kept iff byte 4 (i mod 4) + (j mod 4) of Philox4x32-10 with counter
+ * (j / 4, i / 4, bh, offset mod 2^32) and key (seed mod 2^32, seed / 2^32)
+ * is >= p8 (byte b of the output is bits 8 (b mod 4) .. +7 of word b / 4).
+ * mask: [n_q, n_kv] bytes, 1 = kept.
+ */
+int fa_oracle_dropout_mask(uint64_t seed, uint64_t offset, int64_t bh, int64_t n_q, int64_t n_kv,
+                           int p8, uint8_t *mask)
+{
+    if (!mask || n_q < 0 || n_kv < 0 || bh < 0 || p8 < 0 || p8 > 255) return 1;
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    for (int64_t i = 0; i < n_q; ++i)
+        for (int64_t j = 0; j < n_kv; ++j) {
+            const uint32_t ctr[4] = {(uint32_t)(j / 4), (uint32_t)(i / 4), (uint32_t)bh, (uint32_t)offset};
+            uint32_t out[4];
+            fa_oracle_philox4x32_10(ctr, key, out);
+            const unsigned byte = (out[i % 4] >> (8 * (j % 4))) & 0xFFu;
+            mask[i * n_kv + j] = byte >= (unsigned)p8 ? 1 : 0;
+        }
+    return 0;
+}
+
+/*
+ * Attention with dropout for one (batch, head) slice: P as in
+ * fa_oracle_naive (three passes over the visible keys), then
+ *   O_i = rescale * sum_j P_ij keep_ij v_j,   LSE_i = m_i + ln l_i
+ * (the LSE is that of the scores, before dropout).  keep: [n_q, n_kv]
+ * bytes; rescale = 1 / (1 - p8 / 256) is passed in.
+ */
+int fa_oracle_attention_dropout(const double *q, const double *k, const double *v, int64_t n_q,
+                                int64_t n_kv, int64_t d, double scale, int causal,
+                                const uint8_t *keep, double rescale, double *o, double *lse)
+{
+    if (!q || !k || !v || !keep || !o || !lse || n_q < 0 || n_kv < 1 || d < 1) return 1;
+    int status = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)n_kv * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            status = 2;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < n_q; ++i) {
+            if (!s) continue;
+            const int64_t nv = visible_keys(i, n_kv, causal);
+            double m = -INFINITY;
+            for (int64_t j = 0; j < nv; ++j) {
+                s[j] = score(q + i * d, k + j * d, d, scale);
+                if (s[j] > m) m = s[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < nv; ++j) l += exp(s[j] - m);
+            double *oi = o + i * d;
+            for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+            for (int64_t j = 0; j < nv; ++j) {
+                if (!keep[i * n_kv + j]) continue;
+                const double zij = rescale * exp(s[j] - m) / l;
+                for (int64_t c = 0; c < d; ++c) oi[c] += zij * v[j * d + c];
+            }
+            lse[i] = m + log(l);
+        }
+        free(s);
+    }
+    return status;
+}
+
+/*
+ * Gradients of fa_oracle_attention_dropout for one slice (textbook, as
+ * fa_oracle_backward, with Z_ij = rescale * keep_ij):
+ *   dV_j = sum_i P_ij Z_ij dO_i,   dP_ij = Z_ij (dO_i . v_j),
+ *   D_i = sum_j P_ij dP_ij,        dS_ij = P_ij (dP_ij - D_i),
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+ * Whole slices: dq [n_q, d], dk, dv [n_kv, d].
+ */
+int fa_oracle_backward_dropout(const double *q, const double *k, const double *v, const double *dout,
+                               int64_t n_q, int64_t n_kv, int64_t d, double scale, int causal,
+                               const uint8_t *keep, double rescale, double *dq, double *dk, double *dv)
+{
+    if (!q || !k || !v || !dout || !keep || !dq || !dk || !dv || n_q < 0 || n_kv < 1 || d < 1) return 1;
+    double *P = (double *)calloc((size_t)(n_q ? n_q : 1) * (size_t)n_kv, sizeof(double));
+    double *dS = (double *)calloc((size_t)(n_q ? n_q : 1) * (size_t)n_kv, sizeof(double));
+    if (!P || !dS) {
+        free(P); free(dS);
+        return 2;
+    }
+    /* per row: P, dP, D, dS and dQ */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < n_q; ++i) {
+        const int64_t nv = visible_keys(i, n_kv, causal);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nv; ++j) {
+            P[i * n_kv + j] = score(q + i * d, k + j * d, d, scale);
+            if (P[i * n_kv + j] > m) m = P[i * n_kv + j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < nv; ++j) l += exp(P[i * n_kv + j] - m);
+        for (int64_t j = 0; j < nv; ++j) P[i * n_kv + j] = exp(P[i * n_kv + j] - m) / l;
+        double Di = 0.0;
+        for (int64_t j = 0; j < nv; ++j) {
+            double dpt = 0.0;
+            for (int64_t c = 0; c < d; ++c) dpt += dout[i * d + c] * v[j * d + c];
+            const double dpij = keep[i * n_kv + j] ? rescale * dpt : 0.0;
+            dS[i * n_kv + j] = dpij;
+            Di += P[i * n_kv + j] * dpij;
+        }
+        for (int64_t c = 0; c < d; ++c) dq[i * d + c] = 0.0;
+        for (int64_t j = 0; j < nv; ++j) {
+            dS[i * n_kv + j] = P[i * n_kv + j] * (dS[i * n_kv + j] - Di);
+            for (int64_t c = 0; c < d; ++c) dq[i * d + c] += dS[i * n_kv + j] * k[j * d + c];
+        }
+        for (int64_t c = 0; c < d; ++c) dq[i * d + c] *= scale;
+    }
+    /* per key: dV and dK (P and dS are zero where key j is not visible) */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t j = 0; j < n_kv; ++j) {
+        for (int64_t c = 0; c < d; ++c) {
+            dk[j * d + c] = 0.0;
+            dv[j * d + c] = 0.0;
+        }
+        for (int64_t i = 0; i < n_q; ++i) {
+            const double zij = keep[i * n_kv + j] ? rescale * P[i * n_kv + j] : 0.0;
+            for (int64_t c = 0; c < d; ++c) {
+                dv[j * d + c] += zij * dout[i * d + c];
+                dk[j * d + c] += dS[i * n_kv + j] * q[i * d + c];
+            }
+        }
+        for (int64_t c = 0; c < d; ++c) dk[j * d + c] *= scale;
+    }
+    free(P); free(dS);
+    return 0;
+}
+
+/*
  * OCP 8-bit floating point E4M3 ("fn" variant) to double: 1 sign bit,
  * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes
  * subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN and there are no
