@@ -540,7 +540,7 @@ int fa_oracle_attention_dropout(const double *q, const double *k, const double *
                 if (s[j] > m) m = s[j];
             }
             double l = 0.0;
-            for (int64_t j = 0; j < nv; ++j) l += exp(s[j] - m);
+            for (int64_t j = 0; j < nv; ++j) l = l + exp(s[j] - m);
             double *oi = o + i * d;
             for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
             for (int64_t j = 0; j < nv; ++j) {
