@@ -68,6 +68,14 @@ double score_factor(const fa_fwd_args *a) {
 
 const int64_t kMaxRows = (int64_t)1 << 30;
 
+// Dropout probability quantised to p8 / 256 (0 = no dropout); -1 if p is not
+// in [0, 1).
+int dropout_p8(float p) {
+    if (!(p >= 0.0f && p < 1.0f)) return -1;
+    double x = floor((double)p * 256.0 + 0.5);
+    return (int)(x > 255.0 ? 255.0 : x);
+}
+
 }  // namespace
 
 extern "C" int fa_validate(const fa_fwd_args *a) {
@@ -87,6 +95,9 @@ extern "C" int fa_validate(const fa_fwd_args *a) {
         (!isfinite(a->descale_q) || !isfinite(a->descale_k) || !isfinite(a->descale_v)))
         return FA_ERR_SCALE;
     if (!isfinite((float)score_factor(a))) return FA_ERR_SCALE;
+    const int p8 = dropout_p8(a->dropout_p);
+    if (p8 < 0) return FA_ERR_DROPOUT;
+    if (p8 > 0 && ((a->dtype != FA_BF16 && a->dtype != FA_F16) || a->d > 128)) return FA_ERR_DROPOUT;
     if (fa_num_variants(a->dtype, a->d, a->causal) == 0) return FA_ERR_HEAD_DIM;
     if (a->tile_override < 0 || a->tile_override > fa_num_variants(a->dtype, a->d, a->causal))
         return FA_ERR_VARIANT;
@@ -141,7 +152,8 @@ extern "C" const char *fa_strerror(int status) {
         case FA_ERR_DEVICE: return "no usable gfx950 device";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_VARIANT: return "no compiled variant for this problem (or tile_override out of range)";
-        case FA_ERR_WORKSPACE: return "split-KV workspace NULL, misaligned or too small";
+        case FA_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
+        case FA_ERR_DROPOUT: return "dropout_p outside [0, 1), or dropout not supported here (fp16/bf16, d <= 128, not split-KV)";
         default: return "unknown status";
     }
 }
@@ -194,6 +206,11 @@ extern "C" int fa_fwd_ex(const fa_fwd_args *a) {
     p.kv_split = (int)a->N_kv;
     p.part_o = nullptr;
     p.part_lse = nullptr;
+    p.p8 = (unsigned)dropout_p8(a->dropout_p);
+    p.seed_lo = (unsigned)a->dropout_seed;
+    p.seed_hi = (unsigned)(a->dropout_seed >> 32);
+    p.drop_off = (unsigned)a->dropout_offset;
+    if (p.p8 != 0) p.o_mul = (float)(256.0 / (256.0 - p.p8));
     (void)hipGetLastError();  // clear a stale error so it is not reported as ours
     return v->launch(p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -253,6 +270,7 @@ int validate_split(const fa_fwd_args *a, int num_splits) {
     const int st = fa_validate(a);
     if (st != FA_OK) return st;
     if (num_splits < 0) return FA_ERR_SHAPE;
+    if (dropout_p8(a->dropout_p) != 0) return FA_ERR_DROPOUT;
     const int nv = count_variants(a->dtype, a->d, a->causal, 1);
     if (nv == 0) return FA_ERR_VARIANT;
     if (a->tile_override > nv) return FA_ERR_VARIANT;
@@ -308,6 +326,8 @@ extern "C" int fa_fwd_splitkv(const fa_fwd_args *a, int num_splits, void *worksp
     p.neg = a->scale < 0 ? 1 : 0;
     p.n_split = n_split;
     p.kv_split = kv_split;
+    p.p8 = 0;
+    p.seed_lo = p.seed_hi = p.drop_off = 0;
     p.part_o = (float *)workspace;
     p.part_lse = (float *)((char *)workspace + align256((int64_t)n_split * rows * a->d * 4));
     (void)hipGetLastError();
@@ -346,6 +366,7 @@ extern "C" int fa_bwd_validate(const fa_bwd_args *a) {
         return FA_ERR_SHAPE;
     if (!isfinite(a->scale) || !isfinite((float)((double)a->scale * 1.4426950408889634)))
         return FA_ERR_SCALE;
+    if (dropout_p8(a->dropout_p) < 0) return FA_ERR_DROPOUT;
     if (!find_bwd(a->dtype, a->d, a->causal)) return FA_ERR_HEAD_DIM;
     if (bh == 0) return FA_OK;  // nothing to read or write
     if (!a->K || !a->V || !a->dK || !a->dV) return FA_ERR_NULL;
@@ -410,6 +431,28 @@ extern "C" int fa_bwd(const fa_bwd_args *a, void *workspace, int64_t workspace_b
     p.n_kv = (int)a->N_kv;
     p.c = (float)((double)a->scale * 1.4426950408889634);
     p.scale = a->scale;
+    p.p8 = (unsigned)dropout_p8(a->dropout_p);
+    p.seed_lo = (unsigned)a->dropout_seed;
+    p.seed_hi = (unsigned)(a->dropout_seed >> 32);
+    p.drop_off = (unsigned)a->dropout_offset;
+    p.drop_scale = p.p8 ? (float)(256.0 / (256.0 - p.p8)) : 1.0f;
     (void)hipGetLastError();
     return v->launch(p, a->stream) == 0 ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_dropout_mask(float dropout_p, uint64_t dropout_seed, uint64_t dropout_offset, int64_t BH,
+                               int64_t N_q, int64_t N_kv, uint8_t *mask, void *stream) {
+    if (BH < 0 || N_q < 0 || N_kv < 0) return FA_ERR_SHAPE;
+    if (BH > INT32_MAX || N_q > kMaxRows || N_kv > kMaxRows) return FA_ERR_SHAPE;
+    if (BH > 0 && N_q > 0 && N_kv > INT64_MAX / BH / N_q) return FA_ERR_SHAPE;
+    const int p8 = dropout_p8(dropout_p);
+    if (p8 < 0) return FA_ERR_DROPOUT;
+    if (BH * N_q * N_kv == 0) return FA_OK;
+    if (!mask) return FA_ERR_NULL;
+    if (!device_ok()) return FA_ERR_DEVICE;
+    (void)hipGetLastError();
+    return fa::launch_dropout_mask((unsigned)p8, (unsigned)dropout_seed, (unsigned)(dropout_seed >> 32),
+                                   (unsigned)dropout_offset, BH, N_q, N_kv, mask, stream) == 0
+               ? FA_OK
+               : FA_ERR_LAUNCH;
 }

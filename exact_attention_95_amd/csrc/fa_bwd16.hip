@@ -32,11 +32,12 @@ namespace {
 
 constexpr int kBwdTile = 64;  // rows per streamed tile (keys for dQ, queries for dK/dV)
 
-template <typename T_, int D_, int NW_, bool CAUSAL_>
+// DROP: the dropout keep mask of the forward is replayed.
+template <typename T_, int D_, int NW_, bool CAUSAL_, bool DROP_ = false>
 struct CfgB {
     typedef T_ T;
     static constexpr int D = D_, NW = NW_, BC = kBwdTile, NT = NW * 64, BR = 32 * NW;
-    static constexpr bool CAUSAL = CAUSAL_;
+    static constexpr bool CAUSAL = CAUSAL_, DROP = DROP_;
     static constexpr int RB = D * 2, NC = RB / 16, RPB = RB >= 256 ? 1 : 256 / RB;
     static constexpr int KX = (NC < 16 ? NC : 16) - 1, VX = (NC / 4 < 4 ? NC / 4 : 4) - 1;
     static constexpr int TILE = BC * RB;
@@ -206,6 +207,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     const float lse2 = p.lse[row] * kLog2e;
     const float dlt = p.delta[row];
     const float c = p.c;
+    DropRow dr{};
+    if (C::DROP) dr = DropRow{p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi,
+                              (unsigned)qi & 3u};
 
     const int koff_k = row_offset_v<C>(lane);
     const int koff_v = l32 * C::RB + 16 * (h ^ kswz<C>(l32));
@@ -236,6 +240,12 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
+                // dropout: dP of a dropped element is 0, a kept one is scaled
+                unsigned keep = 0xFFu;
+                if (C::DROP) {
+                    const int kbase = t * C::BC + 32 * kb + 16 * k2 + 4 * h;
+                    keep = keep4(dr, kbase) | (keep4(dr, kbase + 8) << 4);
+                }
                 v8 x;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -245,7 +255,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
                         const int key = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                         pr = key < lim ? pr : 0.f;
                     }
-                    x[e] = (T)(pr * (dp[kb][r] - dlt));
+                    const float dpz = C::DROP ? (((keep >> e) & 1u) ? dp[kb][r] * p.drop_scale : 0.f) : dp[kb][r];
+                    x[e] = (T)(pr * (dpz - dlt));
                 }
                 ds[kb][k2] = x;
             }
@@ -321,6 +332,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     load_rows<C>(p.k + (int64_t)bh * n_kv * C::RB, kj, n_kv, kf, h);
     load_rows<C>(p.v + (int64_t)bh * n_kv * C::RB, kj, n_kv, vf, h);
     const float c = p.c;
+    DropCol dc{};
+    if (C::DROP) dc = DropCol{p.p8, (unsigned)kj >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi,
+                              8u * ((unsigned)kj & 3u)};
     const int koff = row_offset_v<C>(lane);
     int voff[C::NVO];
     tr_offsets<C>(lane, voff);
@@ -339,6 +353,11 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             // rows 32 kb + 16 k2 + 8 (e/4) + 4 h + e%4 of the tile
+            unsigned keep = 0xFFu;
+            if (C::DROP) {
+                const int qbase = t * C::BC + 32 * kb + 16 * k2 + 4 * h;
+                keep = keep4_rows(dc, qbase) | (keep4_rows(dc, qbase + 8) << 4);
+            }
             const f32x4 l_lo = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 4 * h);
             const f32x4 l_hi = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 8 + 4 * h);
             const f32x4 d_lo = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 4 * h);
@@ -355,8 +374,11 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
                     const int q = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                     pr = (q < n_q && (!C::CAUSAL || kj <= q)) ? pr : 0.f;
                 }
-                xp[e] = (T)pr;
-                xs[e] = (T)(pr * (dp[r] - dl));
+                // dropout: P o keep for dV (the 1/(1-p) goes into the dV store),
+                // dP of a dropped element 0 and of a kept one scaled
+                const bool kept = !C::DROP || ((keep >> e) & 1u);
+                xp[e] = (T)(kept ? pr : 0.f);
+                xs[e] = (T)(pr * ((C::DROP ? (kept ? dp[r] * p.drop_scale : 0.f) : dp[r]) - dl));
             }
             pb[k2] = xp;
             ds[k2] = xs;
@@ -458,14 +480,14 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     if (kj < n_kv) {
         const int64_t row = (int64_t)bh * n_kv + kj;
         store_rows<C>(p.dk + row * C::RB, dk, p.scale, h);
-        store_rows<C>(p.dv + row * C::RB, dv, 1.f, h);
+        store_rows<C>(p.dv + row * C::RB, dv, C::DROP ? p.drop_scale : 1.f, h);
     }
 }
 
-template <typename T, int D, int NWQ, int NWK, bool CAUSAL>
-int launch_bwd(const BwdParams &p, void *stream) {
-    typedef CfgB<T, D, NWQ, CAUSAL> CQ;
-    typedef CfgB<T, D, NWK, CAUSAL> CK;
+template <typename T, int D, int NWQ, int NWK, bool CAUSAL, bool DROP>
+int launch_bwd_t(const BwdParams &p, void *stream) {
+    typedef CfgB<T, D, NWQ, CAUSAL, DROP> CQ;
+    typedef CfgB<T, D, NWK, CAUSAL, DROP> CK;
     hipStream_t st = (hipStream_t)stream;
     const int64_t rows = (int64_t)p.n_bh * p.n_q;
     if (rows > 0) {
@@ -480,7 +502,47 @@ int launch_bwd(const BwdParams &p, void *stream) {
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
+template <typename T, int D, int NWQ, int NWK, bool CAUSAL>
+int launch_bwd(const BwdParams &p, void *stream) {
+    return p.p8 != 0 ? launch_bwd_t<T, D, NWQ, NWK, CAUSAL, true>(p, stream)
+                     : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
+}
+
+// The dropout keep mask as bytes, one 4 x 4 block of one slice per thread
+// (one Philox call).
+__global__ __launch_bounds__(256) void dropout_mask_kernel(unsigned p8, unsigned k0, unsigned k1, unsigned off,
+                                                           int64_t n_bh, int64_t n_q, int64_t n_kv,
+                                                           unsigned char *mask) {
+    const int64_t qb = (n_q + 3) / 4, kb = (n_kv + 3) / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n_bh * qb * kb) return;
+    const int64_t bh = idx / (qb * kb);
+    const int64_t rest = idx - bh * qb * kb;
+    const int64_t i4 = rest / kb, j4 = rest - (rest / kb) * kb;
+    unsigned out[4];
+    philox4x32_10((unsigned)j4, (unsigned)i4, (unsigned)bh, off, k0, k1, out);
+    for (int a = 0; a < 4; ++a) {
+        const int64_t i = 4 * i4 + a;
+        if (i >= n_q) break;
+        for (int b = 0; b < 4; ++b) {
+            const int64_t j = 4 * j4 + b;
+            if (j >= n_kv) break;
+            const unsigned byte = (out[a] >> (8 * b)) & 0xFFu;
+            mask[(bh * n_q + i) * n_kv + j] = (p8 == 0 || byte >= p8) ? 1 : 0;
+        }
+    }
+}
+
 }  // namespace
+
+int launch_dropout_mask(unsigned p8, unsigned seed_lo, unsigned seed_hi, unsigned off, int64_t n_bh,
+                        int64_t n_q, int64_t n_kv, unsigned char *mask, void *stream) {
+    const int64_t n = n_bh * ((n_q + 3) / 4) * ((n_kv + 3) / 4);
+    if (n == 0) return 0;
+    hipLaunchKernelGGL(dropout_mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, p8, seed_lo, seed_hi, off, n_bh, n_q, n_kv, mask);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 #define FA_B16(T, DT, D, NWQ, NWK, CAUSAL)                                                  \
     BwdVariant{DT, D, CAUSAL, "dq_w" #NWQ "_dkdv_w" #NWK, &launch_bwd<T, D, NWQ, NWK, CAUSAL>}

@@ -73,6 +73,31 @@ __device__ __forceinline__ i32x2v lds_read_tr8(const void *p) {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2v *)p);
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011): ten rounds of two 32x32->64-bit products
+// with the multipliers 0xD2511F53 and 0xCD9E8D57, the words recombined as
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0), the key bumped by the Weyl
+// constants 0x9E3779B9 and 0xBB67AE85 after each round.
+__device__ __forceinline__ void philox4x32_10(unsigned c0, unsigned c1, unsigned c2, unsigned c3, unsigned k0,
+                                              unsigned k1, unsigned (&out)[4]) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const unsigned hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const unsigned hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const unsigned n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
 // Maps the hardware workgroup index to a logical one so that consecutive
 // logical indices (the query blocks of one head) land on the same XCD:
 // workgroups are dispatched to the 8 XCDs round-robin, and each XCD has its

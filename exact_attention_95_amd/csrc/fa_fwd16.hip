@@ -43,11 +43,13 @@ namespace {
 
 // SPLIT: the workgroup covers one chunk of the key range (split-KV) and
 // writes a float32 partial output and LSE instead of O.
-template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_, bool SPLIT_ = false>
+// DROP: P is multiplied by the dropout keep mask before the PV product.
+template <typename T_, int D_, int NW_, int BC_, bool CAUSAL_, bool SPLIT_ = false, bool DROP_ = false>
 struct Cfg {
     typedef T_ T;
     static constexpr int D = D_, NW = NW_, BC = BC_, NT = NW * 64, BR = 32 * NW;
-    static constexpr bool SPLIT = SPLIT_;
+    static constexpr bool SPLIT = SPLIT_, DROP = DROP_;
+    typedef Cfg<T_, D_, NW_, BC_, CAUSAL_, SPLIT_, true> WithDrop;
     // waves per SIMD the register budget must allow (the split kernels are
     // bound by HBM and want two workgroups of 4 waves in flight per CU)
     static constexpr int MIN_WAVES = SPLIT_ ? 2 : 1;
@@ -95,7 +97,7 @@ template <class C>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
                                              typename Mma16<typename C::T>::v8 (&pb)[C::KB][2],
                                              float &m_use, float &l_acc, float &alpha, bool &raised,
-                                             float c) {
+                                             float c, const DropRow &dr = DropRow{}, int t0 = 0) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     typedef typename C::T T;
@@ -112,16 +114,23 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
     m_use = m_new;
     const float mref = (m_use == kNegInf) ? 0.f : m_use;
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
+    const int h = lane_id() >> 5;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
+            // register 8 k2 + e holds key t0 + 32 kb + 8 (2 k2 + e/4) + 4 h + e%4
+            unsigned keep = 0xFFu;
+            if (C::DROP) {
+                const int kbase = t0 + 32 * kb + 16 * k2 + 4 * h;
+                keep = keep4(dr, kbase) | (keep4(dr, kbase + 8) << 4);
+            }
             v8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * k2 + e], c, -mref));
-                l4[e & 3] += v;
-                x[e] = (T)v;
+                l4[e & 3] += v;  // the row sum is that of the scores, before dropout
+                x[e] = (T)(((keep >> e) & 1u) ? v : 0.f);
             }
             pb[kb][k2] = x;
         }
@@ -262,6 +271,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     float alpha = 1.f;       // pending rescale of O
     bool raised = false;
     const float c = p.c;
+    DropRow dr{};
+    if (C::DROP) dr = DropRow{p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi,
+                              (unsigned)qi & 3u};
     v8 p0[C::KB][2], p1[C::KB][2];  // P of even / odd tiles
 
     wait_vm();
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
         f32x16 s[C::KB];
         qk_tile<C>(s, kbuf(0), koff, qf);
         if (need_mask(0)) mask_tile<C>(s, 0, rqi, n_kv, h);
-        softmax_tile<C>(s, p0, m_use, l_acc, alpha, raised, c);
+        softmax_tile<C>(s, p0, m_use, l_acc, alpha, raised, c, dr, 0);
         raised = false;  // O is still zero
     }
 
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
             schedule_qk<C>();
             if (masked) mask_tile<C>(s, (t + 1) * C::BC, rqi, n_kv, h);
             pv_tile<C>(o, vbuf(PAR), voff, pc);
-            softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c);
+            softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c, dr, (t + 1) * C::BC);
             schedule_pv_softmax<C>();
         } else {
             pv_tile<C>(o, vbuf(PAR), voff, pc);
@@ -343,6 +355,15 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
 
 template <class C>
 int launch(const KParams &p, void *stream) {
+    if (p.p8 != 0) {
+        // dropout instances exist for the single-pass kernels with d <= 128
+        if constexpr (!C::SPLIT && C::D <= 128) {
+            hipLaunchKernelGGL(fwd16_kernel<typename C::WithDrop>, dim3(p.n_wg), dim3(C::NT), 0,
+                               (hipStream_t)stream, p);
+            return hipGetLastError() == hipSuccess ? 0 : 1;
+        }
+        return 1;
+    }
     hipLaunchKernelGGL(fwd16_kernel<C>, dim3(p.n_wg), dim3(C::NT), 0, (hipStream_t)stream, p);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }

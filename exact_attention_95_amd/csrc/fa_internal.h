@@ -29,6 +29,9 @@ struct KParams {
     int kv_split;
     float *part_o;
     float *part_lse;
+    // dropout: p8 = 0 means none; o_mul already includes 256 / (256 - p8)
+    unsigned p8;
+    unsigned seed_lo, seed_hi, drop_off;
 };
 
 // A compiled kernel instance and the query-block height it uses.
@@ -69,6 +72,10 @@ struct BwdParams {
     int n_kv;
     float c;           // scale * log2(e) (signed)
     float scale;       // signed
+    // dropout: p8 = 0 means none; drop_scale = 256 / (256 - p8)
+    unsigned p8;
+    unsigned seed_lo, seed_hi, drop_off;
+    float drop_scale;
 };
 
 // The three backward launches (D, dQ, dK/dV) for one (dtype, d, causal).
@@ -83,5 +90,9 @@ struct BwdVariant {
 };
 
 const BwdVariant *bwd_variants(int *count);
+
+// Writes the dropout keep mask (bytes) of n_bh slices of n_q x n_kv; 0 on success.
+int launch_dropout_mask(unsigned p8, unsigned seed_lo, unsigned seed_hi, unsigned off, int64_t n_bh,
+                        int64_t n_q, int64_t n_kv, unsigned char *mask, void *stream);
 
 }  // namespace fa

@@ -164,4 +164,41 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[C::DB], const char *Vs, cons
             }
 }
 
+// Dropout state of one lane's query row qi: Philox counter words c1 = qi/4,
+// c2 = the (batch, head) index, c3 = offset; key (k0, k1); the lane reads
+// output word qi mod 4 of each call.
+struct DropRow {
+    unsigned p8, c1, c2, c3, k0, k1, word;
+};
+
+// Keep bits of the 4 keys kbase .. kbase + 3 (kbase a multiple of 4) for the
+// lane's row: bit c set iff byte c of the row's word is >= p8.
+__device__ __forceinline__ unsigned keep4(const DropRow &dr, int kbase) {
+    unsigned out[4];
+    philox4x32_10((unsigned)kbase >> 2, dr.c1, dr.c2, dr.c3, dr.k0, dr.k1, out);
+    const unsigned w = dr.word == 0 ? out[0] : dr.word == 1 ? out[1] : dr.word == 2 ? out[2] : out[3];
+    unsigned bits = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bits |= (((w >> (8 * c)) & 0xFFu) >= dr.p8 ? 1u : 0u) << c;
+    return bits;
+}
+
+// Dropout state of one lane's key kj in the key-per-lane layout (dK/dV):
+// counter words c0 = kj/4, c2 = the (batch, head) index, c3 = offset; the
+// lane reads byte kj mod 4 (bits shift .. shift + 7) of every output word.
+struct DropCol {
+    unsigned p8, c0, c2, c3, k0, k1, shift;
+};
+
+// Keep bits of the 4 rows qbase .. qbase + 3 (qbase a multiple of 4) for the
+// lane's key: bit c set iff the key's byte of output word c is >= p8.
+__device__ __forceinline__ unsigned keep4_rows(const DropCol &dc, int qbase) {
+    unsigned out[4];
+    philox4x32_10(dc.c0, (unsigned)qbase >> 2, dc.c2, dc.c3, dc.k0, dc.k1, out);
+    unsigned bits = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bits |= (((out[c] >> dc.shift) & 0xFFu) >= dc.p8 ? 1u : 0u) << c;
+    return bits;
+}
+
 }  // namespace fa

@@ -19,11 +19,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_SCALE,
- FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE) = range(12)
+ FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE, FA_ERR_DROPOUT) = range(13)
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
             "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_bwd",
-            "fa_bwd_validate", "fa_bwd_workspace_bytes")
+            "fa_bwd_validate", "fa_bwd_workspace_bytes", "fa_dropout_mask")
 
 
 class FaFwdArgs(ctypes.Structure):
@@ -38,6 +38,8 @@ class FaFwdArgs(ctypes.Structure):
         ("descale_q", ctypes.c_float), ("descale_k", ctypes.c_float),
         ("descale_v", ctypes.c_float),
         ("stream", ctypes.c_void_p), ("tile_override", ctypes.c_int),
+        ("dropout_p", ctypes.c_float), ("dropout_seed", ctypes.c_uint64),
+        ("dropout_offset", ctypes.c_uint64),
     ]
 
 
@@ -52,6 +54,8 @@ class FaBwdArgs(ctypes.Structure):
         ("N_kv", ctypes.c_int64), ("d", ctypes.c_int64),
         ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("dtype", ctypes.c_int),
         ("stream", ctypes.c_void_p),
+        ("dropout_p", ctypes.c_float), ("dropout_seed", ctypes.c_uint64),
+        ("dropout_offset", ctypes.c_uint64),
     ]
 
 
@@ -98,6 +102,9 @@ def load(path: str = LIB_PATH):
             lib.fa_bwd_validate.argtypes = [ctypes.POINTER(FaBwdArgs)]
             lib.fa_bwd_workspace_bytes.restype = i64
             lib.fa_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FaBwdArgs)]
+            lib.fa_dropout_mask.restype = ctypes.c_int
+            lib.fa_dropout_mask.argtypes = [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, i64, i64,
+                                            i64, vp, vp]
             _lib = lib
         return _lib
 
@@ -147,6 +154,11 @@ def fa_bwd_workspace_bytes(args: FaBwdArgs) -> int:
     return load().fa_bwd_workspace_bytes(ctypes.byref(args))
 
 
+def fa_dropout_mask(dropout_p, seed, offset, BH, N_q, N_kv, mask, stream=None) -> int:
+    return load().fa_dropout_mask(float(dropout_p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
+                                  BH, N_q, N_kv, mask, stream)
+
+
 def _dtype_code(t) -> int:
     import torch
     codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16,
@@ -157,7 +169,7 @@ def _dtype_code(t) -> int:
 
 
 def make_args(q, k, v, o, lse, scale: float, causal: bool, descale=(1.0, 1.0, 1.0),
-              stream=None, tile: int = 0) -> FaFwdArgs:
+              stream=None, tile: int = 0, dropout=(0.0, 0, 0)) -> FaFwdArgs:
     """fa_fwd_args for torch tensors q [B,H,N_q,d], k/v [B,H,N_kv,d], o, lse."""
     B, H, N_q, d = q.shape
     a = FaFwdArgs()
@@ -170,18 +182,23 @@ def make_args(q, k, v, o, lse, scale: float, causal: bool, descale=(1.0, 1.0, 1.
     a.descale_q, a.descale_k, a.descale_v = (float(x) for x in descale)
     a.stream = stream
     a.tile_override = tile
+    a.dropout_p = float(dropout[0])
+    a.dropout_seed = int(dropout[1]) & (2**64 - 1)
+    a.dropout_offset = int(dropout[2]) & (2**64 - 1)
     return a
 
 
 def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None, out=None,
-        lse=None, with_lse: bool = True, stream=None, tile: int = 0):
+        lse=None, with_lse: bool = True, stream=None, tile: int = 0, dropout_p: float = 0.0,
+        seed: int = 0, offset: int = 0):
     """Attention forward of torch device tensors; returns (O, LSE).
 
     q: [B,H,N_q,d]; k, v: [B,H,N_kv,d]; all contiguous, same dtype, on one
     gfx950 device.  scale defaults to 1/sqrt(d) (as float32).  For
     float8_e4m3fn inputs, descale = (descale_q, descale_k, descale_v) and O is
     bfloat16.  ``stream``: a torch stream or raw hipStream_t (default: torch's
-    current stream).
+    current stream).  ``dropout_p``, ``seed``, ``offset``: dropout of P with
+    the library's Philox mask (see include/fa.h).
     """
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -208,7 +225,8 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None,
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    args = make_args(q, k, v, out, lse, scale, causal, descale or (1.0, 1.0, 1.0), stream, tile)
+    args = make_args(q, k, v, out, lse, scale, causal, descale or (1.0, 1.0, 1.0), stream, tile,
+                     (dropout_p, seed, offset))
     with torch.cuda.device(q.device):
         st = fa_fwd_ex(args)
     if st != FA_OK:
@@ -254,7 +272,7 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
 
 
 def make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool,
-                  stream=None) -> FaBwdArgs:
+                  stream=None, dropout=(0.0, 0, 0)) -> FaBwdArgs:
     """fa_bwd_args for torch tensors (shapes as in ``bwd``)."""
     B, H, N_q, d = q.shape
     a = FaBwdArgs()
@@ -267,11 +285,14 @@ def make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool,
     a.causal = int(bool(causal))
     a.dtype = _dtype_code(q)
     a.stream = stream
+    a.dropout_p = float(dropout[0])
+    a.dropout_seed = int(dropout[1]) & (2**64 - 1)
+    a.dropout_offset = int(dropout[2]) & (2**64 - 1)
     return a
 
 
 def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, stream=None,
-        workspace=None):
+        workspace=None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
     """Attention backward of torch device tensors; returns (dQ, dK, dV).
 
     q, o, do: [B,H,N_q,d]; k, v: [B,H,N_kv,d] (bf16 or fp16, contiguous, one
@@ -298,7 +319,8 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, s
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    args = make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream)
+    args = make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream,
+                         (dropout_p, seed, offset))
     need = fa_bwd_workspace_bytes(args)
     if need < 0:
         raise FaError(fa_bwd_validate(args))
@@ -309,3 +331,18 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, s
     if st != FA_OK:
         raise FaError(st)
     return dq, dk, dv
+
+
+def dropout_mask(dropout_p: float, seed: int, offset: int, B: int, H: int, N_q: int, N_kv: int,
+                 device="cuda", stream=None):
+    """The dropout keep mask ([B,H,N_q,N_kv] uint8 on the GPU) the kernels use."""
+    import torch
+    m = torch.empty((B, H, N_q, N_kv), dtype=torch.uint8, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(m.device).cuda_stream
+    with torch.cuda.device(m.device):
+        st = fa_dropout_mask(dropout_p, seed, offset, B * H, N_q, N_kv, m.data_ptr() if m.numel() else None,
+                             stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return m

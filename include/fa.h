@@ -65,7 +65,8 @@ typedef enum {
     FA_ERR_DEVICE = 8,    /* no usable gfx950 device / HIP runtime error before launch */
     FA_ERR_LAUNCH = 9,    /* the kernel launch failed */
     FA_ERR_VARIANT = 10,  /* no compiled variant for this problem / tile_override out of range */
-    FA_ERR_WORKSPACE = 11 /* split-KV workspace NULL, misaligned or too small */
+    FA_ERR_WORKSPACE = 11, /* split-KV or backward workspace NULL, misaligned or too small */
+    FA_ERR_DROPOUT = 12    /* dropout_p outside [0, 1), or dropout where it is not supported */
 } fa_status;
 
 /*
@@ -90,6 +91,22 @@ int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
  * hipStream_t (NULL = null stream).  tile_override selects a compiled tile
  * variant (0 = the library's choice; 1..fa_num_variants() for tuning and
  * cross-checks).
+ *
+ * Dropout ("FlashAttention 与显存" plates 07 and 09 list it among the
+ * operations the fused kernel absorbs; the pages give no generator).
+ * dropout_p in [0, 1) is quantised to p8 / 256 with p8 = floor(256 p + 1/2)
+ * clamped to 255; p8 = 0 means no dropout.  Otherwise
+ *     O_i = 256 / (256 - p8) * sum_j P_ij keep_ij v_j
+ * (LSE stays that of the scores), where keep_ij = 1 iff byte
+ * 4 (i mod 4) + (j mod 4) of Philox4x32-10 (Salmon et al., SC 2011) with
+ * counter (j / 4, i / 4, b H + h, dropout_offset mod 2^32) and key
+ * (dropout_seed mod 2^32, dropout_seed / 2^32) is >= p8; byte k of the four
+ * output words w0..w3 is bits 8 (k mod 4) .. +7 of word k / 4.  i and j are
+ * the row and key indices within the (batch, head).  Supported for FA_F16
+ * and FA_BF16 with d in {64, 128} and the default tile (tile_override 0 or
+ * 1); FA_ERR_DROPOUT otherwise, and from fa_fwd_splitkv.  fa_bwd with the
+ * same dropout_p, dropout_seed and dropout_offset replays the same mask.
+ * fa_dropout_mask writes the mask itself.
  */
 typedef struct {
     const void *Q;
@@ -104,6 +121,9 @@ typedef struct {
     float descale_q, descale_k, descale_v;
     void *stream;
     int tile_override;
+    float dropout_p;         /* 0 = no dropout */
+    uint64_t dropout_seed;
+    uint64_t dropout_offset;
 } fa_fwd_args;
 
 /* Attention forward with the full argument set (see fa_fwd_args). */
@@ -184,6 +204,9 @@ typedef struct {
     int causal;
     int dtype;
     void *stream;   /* hipStream_t; NULL = null stream */
+    float dropout_p;         /* as in fa_fwd_args; must match the forward */
+    uint64_t dropout_seed;
+    uint64_t dropout_offset;
 } fa_bwd_args;
 
 /*
@@ -209,6 +232,19 @@ int64_t fa_bwd_workspace_bytes(const fa_bwd_args *args);
  * repeatable.
  */
 int fa_bwd(const fa_bwd_args *args, void *workspace, int64_t workspace_bytes);
+
+/*
+ * The dropout keep mask of fa_fwd_args (see Dropout above) for BH = B * H
+ * (batch, head) slices of N_q x N_kv: mask[(bh * N_q + i) * N_kv + j] = 1 if
+ * element (i, j) of slice bh is kept, else 0 (all 1 when p8 = 0).  mask:
+ * device memory of BH * N_q * N_kv bytes owned by the caller; runs on
+ * stream (hipStream_t, NULL = null stream).  For tests and for callers that
+ * replay the mask elsewhere.  FA_ERR_SHAPE for negative sizes,
+ * FA_ERR_DROPOUT for dropout_p outside [0, 1), FA_ERR_NULL for a NULL mask
+ * with a non-empty size.
+ */
+int fa_dropout_mask(float dropout_p, uint64_t dropout_seed, uint64_t dropout_offset, int64_t BH,
+                    int64_t N_q, int64_t N_kv, uint8_t *mask, void *stream);
 
 /* Static, never-NULL description of a status code. */
 const char *fa_strerror(int status);

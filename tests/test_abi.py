@@ -255,3 +255,33 @@ def test_bwd_refuses_cpu_tensors():
     lse = torch.zeros(1, 1, 4)
     with pytest.raises(RuntimeError, match="GPU"):
         fa.bwd(q, q, q, q, lse, q)
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 2.0, math.nan, math.inf])
+def test_dropout_probability_is_validated(p):
+    assert fa.fa_validate(good_args(dropout_p=p)) == fa.FA_ERR_DROPOUT
+    assert fa.fa_bwd_validate(good_bwd_args(dropout_p=p)) == fa.FA_ERR_DROPOUT
+    assert fa.fa_dropout_mask(p, 1, 2, 1, 4, 4, None) == fa.FA_ERR_DROPOUT
+
+
+def test_dropout_support_limits():
+    assert fa.fa_validate(good_args(dropout_p=0.1)) == fa.FA_OK
+    assert fa.fa_validate(good_args(dropout_p=0.1, dtype=fa.FA_F16, d=128, causal=1)) == fa.FA_OK
+    assert fa.fa_validate(good_args(dropout_p=0.1, dtype=fa.FA_F32)) == fa.FA_ERR_DROPOUT
+    assert fa.fa_validate(good_args(dropout_p=0.1, d=256)) == fa.FA_ERR_DROPOUT
+    assert fa.fa_validate(good_args(dropout_p=0.1, dtype=fa.FA_FP8_E4M3, d=128)) == fa.FA_ERR_DROPOUT
+    # p quantised to 0 (p < 1/512) is no dropout, accepted everywhere
+    assert fa.fa_validate(good_args(dropout_p=1e-4, dtype=fa.FA_F32)) == fa.FA_OK
+    a = good_args(B=2, H=3, N_q=5, N_kv=1000, d=128, K=0x1000000, V=0x2000000, O=0x3000000,
+                  LSE=0x4000000, dropout_p=0.2)
+    assert fa.fa_splitkv_workspace_bytes(a, 0) == -1
+    assert fa.fa_fwd_splitkv(a, 0, None, 0) == fa.FA_ERR_DROPOUT
+    assert fa.fa_bwd_validate(good_bwd_args(dropout_p=0.3, dropout_seed=2**64 - 1, dropout_offset=7)) == fa.FA_OK
+
+
+def test_dropout_mask_entry_validation():
+    assert fa.fa_dropout_mask(0.1, 1, 2, -1, 4, 4, None) == fa.FA_ERR_SHAPE
+    assert fa.fa_dropout_mask(0.1, 1, 2, 1, -4, 4, None) == fa.FA_ERR_SHAPE
+    assert fa.fa_dropout_mask(0.1, 1, 2, 0, 4, 4, None) == fa.FA_OK
+    assert fa.fa_dropout_mask(0.1, 1, 2, 3, 0, 4, None) == fa.FA_OK
+    assert fa.fa_dropout_mask(0.1, 1, 2, 1, 4, 4, None) == fa.FA_ERR_NULL
