@@ -237,6 +237,9 @@ def main(argv=None) -> int:
                          "choice, -1: off); default: on for workloads with at most 16 query rows")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd: dQ, dK, dV) instead of the forward")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability (Philox mask, seed 1, offset 0) for the forward "
+                         "and --bwd runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
@@ -283,7 +286,7 @@ def main(argv=None) -> int:
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)  # default priority
     fargs = fa.make_args(q, k, v, o, lse, w.sm_scale, w.causal, x["descale"],
-                         stream.cuda_stream, args.tile)
+                         stream.cuda_stream, args.tile, (args.dropout, 1, 0))
     st = fa.fa_validate(fargs)
     if st != fa.FA_OK:
         raise fa.FaError(st)
@@ -315,7 +318,7 @@ def main(argv=None) -> int:
         do = make_dout(w).to(dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         bargs = fa.make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, w.sm_scale, w.causal,
-                                 stream.cuda_stream)
+                                 stream.cuda_stream, (args.dropout, 1, 0))
         bneed = fa.fa_bwd_workspace_bytes(bargs)
         if bneed < 0:
             raise fa.FaError(fa.fa_bwd_validate(bargs))
@@ -379,6 +382,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.n_q, "N_kv": w.n_kv,
                    "d": w.d, "causal": w.causal, "dtype": w.dtype,
+                   "dropout_p": args.dropout,
                    "variant": ("backward" if args.bwd else
                                "split_kv(%s)" % ("auto" if splitkv == 0 else splitkv)
                                if splitkv is not None else
@@ -389,7 +393,7 @@ def main(argv=None) -> int:
                      "traffic": stored_traffic(w.name, w.dtype, args.bwd),
                      "kernel_ms": round(kernel_ms, 4)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.dropout == 0.0:
         rec["cpu_baseline"] = (cpu_baseline_bwd(w, x, do.cpu()) if args.bwd else cpu_baseline(w, x))
     print(json.dumps(rec), flush=True)
     return 0
