@@ -207,9 +207,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     const float lse2 = p.lse[row] * kLog2e;
     const float dlt = p.delta[row];
     const float c = p.c;
-    DropRow dr{};
-    if (C::DROP) dr = DropRow{p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi,
-                              (unsigned)qi & 3u};
+    DropQuad dr{};
+    if (C::DROP) dr = make_drop_quad(p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
 
     const int koff_k = row_offset_v<C>(lane);
     const int koff_v = l32 * C::RB + 16 * (h ^ kswz<C>(l32));
@@ -236,16 +235,20 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         const bool masked = (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
         const int lim = C::CAUSAL ? min(n_kv, qi + 1) : n_kv;
         v8 ds[C::KB][2];
+        // dropout keep bits: keys t BC + 32 kb + 16 k2 + 8 half + 4 h + (0..3)
+        // are block t BC/4 + h + 2 (4 kb + 2 k2 + half)
+        unsigned kq[C::KB] = {};
+        if (C::DROP) {
+#pragma unroll
+            for (int kb = 0; kb < C::KB; ++kb)
+                kq[kb] = drop_group_bits<false>(dr, (unsigned)(t * C::BC >> 2) + h, kb);
+        }
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 // dropout: dP of a dropped element is 0, a kept one is scaled
-                unsigned keep = 0xFFu;
-                if (C::DROP) {
-                    const int kbase = t * C::BC + 32 * kb + 16 * k2 + 4 * h;
-                    keep = keep4(dr, kbase) | (keep4(dr, kbase + 8) << 4);
-                }
+                const unsigned keep = C::DROP ? (kq[kb] >> (8 * k2)) & 0xFFu : 0xFFu;
                 v8 x;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -332,9 +335,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     load_rows<C>(p.k + (int64_t)bh * n_kv * C::RB, kj, n_kv, kf, h);
     load_rows<C>(p.v + (int64_t)bh * n_kv * C::RB, kj, n_kv, vf, h);
     const float c = p.c;
-    DropCol dc{};
-    if (C::DROP) dc = DropCol{p.p8, (unsigned)kj >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi,
-                              8u * ((unsigned)kj & 3u)};
+    DropQuad dc{};
+    if (C::DROP) dc = make_drop_quad(p.p8, (unsigned)kj >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
     const int koff = row_offset_v<C>(lane);
     int voff[C::NVO];
     tr_offsets<C>(lane, voff);
@@ -350,14 +352,13 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     auto elementwise = [&](auto mk, int t, const float *st, int kb, const f32x16 &s, const f32x16 &dp,
                            v8 (&pb)[2], v8 (&ds)[2]) {
         constexpr bool MK = decltype(mk)::value;
+        // dropout keep bits: rows t BC + 32 kb + 16 k2 + 8 half + 4 h + (0..3)
+        // are block t BC/4 + h + 2 (4 kb + 2 k2 + half)
+        const unsigned kq = C::DROP ? drop_group_bits<true>(dc, (unsigned)(t * C::BC >> 2) + h, kb) : 0u;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             // rows 32 kb + 16 k2 + 8 (e/4) + 4 h + e%4 of the tile
-            unsigned keep = 0xFFu;
-            if (C::DROP) {
-                const int qbase = t * C::BC + 32 * kb + 16 * k2 + 4 * h;
-                keep = keep4_rows(dc, qbase) | (keep4_rows(dc, qbase + 8) << 4);
-            }
+            const unsigned keep = C::DROP ? (kq >> (8 * k2)) & 0xFFu : 0xFFu;
             const f32x4 l_lo = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 4 * h);
             const f32x4 l_hi = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 8 + 4 * h);
             const f32x4 d_lo = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 4 * h);

@@ -97,7 +97,7 @@ template <class C>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
                                              typename Mma16<typename C::T>::v8 (&pb)[C::KB][2],
                                              float &m_use, float &l_acc, float &alpha, bool &raised,
-                                             float c, const DropRow &dr = DropRow{}, int t0 = 0) {
+                                             float c, const DropQuad &dq = DropQuad{}, int t0 = 0) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     typedef typename C::T T;
@@ -115,16 +115,19 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[C::KB],
     const float mref = (m_use == kNegInf) ? 0.f : m_use;
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
     const int h = lane_id() >> 5;
+    // keys t0 + 32 kb + 16 k2 + 8 half + 4 h + (0..3) are block t0/4 + h + 2 (4 kb + 2 k2 + half)
+    unsigned kq[C::KB] = {};
+    if (C::DROP) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) kq[kb] = drop_group_bits<false>(dq, (unsigned)(t0 >> 2) + h, kb);
+    }
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             // register 8 k2 + e holds key t0 + 32 kb + 8 (2 k2 + e/4) + 4 h + e%4
             unsigned keep = 0xFFu;
-            if (C::DROP) {
-                const int kbase = t0 + 32 * kb + 16 * k2 + 4 * h;
-                keep = keep4(dr, kbase) | (keep4(dr, kbase + 8) << 4);
-            }
+            if (C::DROP) keep = (kq[kb] >> (8 * k2)) & 0xFFu;
             v8 x;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -271,9 +274,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     float alpha = 1.f;       // pending rescale of O
     bool raised = false;
     const float c = p.c;
-    DropRow dr{};
-    if (C::DROP) dr = DropRow{p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi,
-                              (unsigned)qi & 3u};
+    DropQuad dr{};
+    if (C::DROP) dr = make_drop_quad(p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
     v8 p0[C::KB][2], p1[C::KB][2];  // P of even / odd tiles
 
     wait_vm();

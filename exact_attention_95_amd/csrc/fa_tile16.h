@@ -164,41 +164,87 @@ __device__ __forceinline__ void pv_tile(f32x16 (&o)[C::DB], const char *Vs, cons
             }
 }
 
-// Dropout state of one lane's query row qi: Philox counter words c1 = qi/4,
-// c2 = the (batch, head) index, c3 = offset; key (k0, k1); the lane reads
-// output word qi mod 4 of each call.
-struct DropRow {
-    unsigned p8, c1, c2, c3, k0, k1, word;
+// Dropout mask bits, shared across the four lanes of a quad.  The mask of
+// element (row i, key j) is byte 4 (i mod 4) + (j mod 4) of the Philox4x32-10
+// output for counter (j / 4, i / 4, batch-head index, offset), compared with
+// p8; one call therefore covers a 4 x 4 block of rows and keys.  In both
+// register layouts the four lanes of a quad hold four consecutive indices of
+// the same block (four rows in the query-per-lane layout, four keys in the
+// key-per-lane layout) and need the same blocks, so each lane computes one
+// block of every four and the quad exchanges the resulting 16 keep bits with
+// DPP moves.
+struct DropQuad {
+    unsigned pp, plo;         // p8 in every byte, and its low 7 bits in every byte
+    unsigned fixed, c2, c3;   // the quad's own block index (row or key), batch-head, offset
+    unsigned k0, k1;          // Philox key (seed)
+    unsigned r;               // lane & 3: the lane's row or key within the block
 };
 
-// Keep bits of the 4 keys kbase .. kbase + 3 (kbase a multiple of 4) for the
-// lane's row: bit c set iff byte c of the row's word is >= p8.
-__device__ __forceinline__ unsigned keep4(const DropRow &dr, int kbase) {
-    unsigned out[4];
-    philox4x32_10((unsigned)kbase >> 2, dr.c1, dr.c2, dr.c3, dr.k0, dr.k1, out);
-    const unsigned w = dr.word == 0 ? out[0] : dr.word == 1 ? out[1] : dr.word == 2 ? out[2] : out[3];
-    unsigned bits = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bits |= (((w >> (8 * c)) & 0xFFu) >= dr.p8 ? 1u : 0u) << c;
-    return bits;
+__device__ __forceinline__ DropQuad make_drop_quad(unsigned p8, unsigned fixed, unsigned bh, unsigned off,
+                                                   unsigned seed_lo, unsigned seed_hi) {
+    DropQuad q;
+    q.pp = p8 * 0x01010101u;
+    q.plo = q.pp & 0x7F7F7F7Fu;
+    q.fixed = fixed;
+    q.c2 = bh;
+    q.c3 = off;
+    q.k0 = seed_lo;
+    q.k1 = seed_hi;
+    q.r = lane_id() & 3u;
+    return q;
 }
 
-// Dropout state of one lane's key kj in the key-per-lane layout (dK/dV):
-// counter words c0 = kj/4, c2 = the (batch, head) index, c3 = offset; the
-// lane reads byte kj mod 4 (bits shift .. shift + 7) of every output word.
-struct DropCol {
-    unsigned p8, c0, c2, c3, k0, k1, shift;
-};
-
-// Keep bits of the 4 rows qbase .. qbase + 3 (qbase a multiple of 4) for the
-// lane's key: bit c set iff the key's byte of output word c is >= p8.
-__device__ __forceinline__ unsigned keep4_rows(const DropCol &dc, int qbase) {
-    unsigned out[4];
-    philox4x32_10(dc.c0, (unsigned)qbase >> 2, dc.c2, dc.c3, dc.k0, dc.k1, out);
-    unsigned bits = 0;
+// Keep bits of one 4 x 4 block: bit 4 w + c is set iff byte c of word w is
+// >= p8.  The four byte comparisons of a word run in one register: with h the
+// high bit of each byte, (x | h) - (p & ~h) leaves in each byte's high bit
+// whether x's low 7 bits are >= p's, which decides when the high bits agree;
+// otherwise x's own high bit does.  Multiplying the four high bits by
+// 2^0 + 2^7 + 2^14 + 2^21 lands bit c of the word at bit 28 + c with no
+// other term at or above bit 28.
+__device__ __forceinline__ unsigned drop_block_bits(const unsigned (&out)[4], const DropQuad &q) {
+    unsigned b = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) bits |= (((out[c] >> dc.shift) & 0xFFu) >= dc.p8 ? 1u : 0u) << c;
-    return bits;
+    for (int w = 0; w < 4; ++w) {
+        const unsigned x = out[w];
+        const unsigned t = (x | 0x80808080u) - q.plo;
+        const unsigned m = x ^ q.pp;
+        const unsigned ge = ((m & x) | (~m & t)) & 0x80808080u;
+        b |= ((ge * 0x00204081u) >> 28) << (4 * w);
+    }
+    return b;
+}
+
+// Keep bits of the lane for the 4 blocks base + 2 (4 g + i), i = 0 .. 3, along
+// the varying index (keys for COL = false, rows for COL = true): bits
+// 4 i .. 4 i + 3 hold the 4 elements of block i in increasing order of the
+// varying index.  Lane r of the quad computes block i = r.
+template <bool COL>
+__device__ __forceinline__ unsigned drop_group_bits(const DropQuad &q, unsigned base, unsigned g) {
+    const unsigned blk = base + 2u * (4u * g + q.r);
+    unsigned out[4];
+    if (COL)
+        philox4x32_10(q.fixed, blk, q.c2, q.c3, q.k0, q.k1, out);
+    else
+        philox4x32_10(blk, q.fixed, q.c2, q.c3, q.k0, q.k1, out);
+    const unsigned b16 = drop_block_bits(out, q);
+    unsigned v[4];
+    v[0] = b16;
+    // quad_perm patterns of lane xor 1, 2, 3
+    v[1] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)b16, 0xB1, 0xF, 0xF, true);
+    v[2] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)b16, 0x4E, 0xF, 0xF, true);
+    v[3] = (unsigned)__builtin_amdgcn_update_dpp(0, (int)b16, 0x1B, 0xF, 0xF, true);
+    unsigned keep = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        // v[k] came from lane r ^ k, which computed block r ^ k of the group
+        unsigned nib;
+        if (COL)  // the lane's key is byte r: bits r, 4 + r, 8 + r, 12 + r
+            nib = ((((v[k] >> q.r) & 0x1111u) * 0x1248u) >> 12) & 0xFu;
+        else      // the lane's row is word r: bits 4 r .. 4 r + 3
+            nib = (v[k] >> (4u * q.r)) & 0xFu;
+        keep |= nib << (4u * (q.r ^ (unsigned)k));
+    }
+    return keep;
 }
 
 }  // namespace fa
