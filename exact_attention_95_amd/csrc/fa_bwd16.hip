@@ -99,39 +99,68 @@ __device__ __forceinline__ void store_rows(char *rowp, const f32x16 (&acc)[C::DB
         }
 }
 
-// One 32-row block of qk_tile: s = A B with A the block's rows (LDS, row
-// reads from koff0) and B this lane's register row f.
+// Two products of one 32-row block: s = A f and dp = G g, with A and G the
+// block's rows of two LDS tiles (row reads from koff0) and f, g this lane's
+// register rows.  Every operand read is issued before the first MFMA, in a
+// scheduling region of its own: left to itself the scheduler places each read
+// right before its MFMA and reuses one register set, which exposes the LDS
+// latency on every MFMA.  The two accumulation chains alternate.
 template <class C>
-__device__ __forceinline__ void qk_rows(f32x16 &s, const char *blk, int koff0,
-                                        const typename Mma16<typename C::T>::v8 (&f)[C::KS]) {
+__device__ __forceinline__ void qk_rows2(f32x16 &s, f32x16 &dp, const char *ablk, const char *gblk, int koff0,
+                                         const typename Mma16<typename C::T>::v8 (&f)[C::KS],
+                                         const typename Mma16<typename C::T>::v8 (&g)[C::KS]) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     asm volatile("" : "+v"(koff0));
-    s = (f32x16){};
+    v8 a[C::KS], b[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-        const v8 a = *(const v8 *)(blk + (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3));
-        s = M::mma(a, f[ks], s);
+        const int o = (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3);
+        a[ks] = *(const v8 *)(ablk + o);
+        b[ks] = *(const v8 *)(gblk + o);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s = (f32x16){};
+    dp = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        s = M::mma(a[ks], f[ks], s);
+        dp = M::mma(b[ks], g[ks], dp);
     }
 }
 
-// One 32-row block of pv_tile: o^T += A^T B with A the block's rows (LDS,
-// transposed reads) and B = pb (the block's accumulator rows as packed
-// operands, k2 = 0, 1).
+// Two products of one 32-row block of pv_tile: o1^T += A1^T p1 and
+// o2^T += A2^T p2, with A1, A2 the block's rows of two LDS tiles (transposed
+// reads) and p1, p2 the block's packed operands (k2 = 0, 1).  Reads first, in
+// their own scheduling region, as in qk_rows2.
 template <class C>
-__device__ __forceinline__ void pv_rows(f32x16 (&o)[C::DB], const char *blk, const int (&voff)[C::NVO],
-                                        const typename Mma16<typename C::T>::v8 (&pb)[2]) {
+__device__ __forceinline__ void pv_rows2(f32x16 (&o1)[C::DB], const char *blk1,
+                                         const typename Mma16<typename C::T>::v8 (&p1)[2], f32x16 (&o2)[C::DB],
+                                         const char *blk2, const typename Mma16<typename C::T>::v8 (&p2)[2],
+                                         const int (&voff)[C::NVO]) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
+    v8 a1[2][C::DB], a2[2][C::DB];
+    auto rd = [&](const char *base) {
+        const i16x4 lo = lds_read_tr16(base);
+        const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+        return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const char *base = blk + 16 * k2 * C::RB + voff[db & 3] + 256 * (db >> 2);
-            const i16x4 lo = lds_read_tr16(base);
-            const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
-            const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = M::mma(a, pb[k2], o[db]);
+            const int off = 16 * k2 * C::RB + voff[db & 3] + 256 * (db >> 2);
+            a1[k2][db] = rd(blk1 + off);
+            a2[k2][db] = rd(blk2 + off);
+        }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            o1[db] = M::mma(a1[k2][db], p1[k2], o1[db]);
+            o2[db] = M::mma(a2[k2][db], p2[k2], o2[db]);
         }
 }
 
@@ -398,48 +427,28 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         v8 pb[2][2], ds[2][2];
         constexpr int NQK = 2 * C::KS, NPV = 4 * C::DB;  // MFMAs of two products, per block
         // segment A: S, dP of block 0
-        qk_rows<C>(s[0], qt, koff, kf);
-        qk_rows<C>(dp[0], gt, koff, vf);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < NQK; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        qk_rows2<C>(s[0], dp[0], qt, gt, koff, kf, vf);
         __builtin_amdgcn_sched_barrier(0);
         // segment B: S, dP of block 1 under the VALU of block 0
-        qk_rows<C>(s[1], qt + 32 * C::RB, koff, kf);
-        qk_rows<C>(dp[1], gt + 32 * C::RB, koff, vf);
+        qk_rows2<C>(s[1], dp[1], qt + 32 * C::RB, gt + 32 * C::RB, koff, kf, vf);
         elementwise(mk, t, st, 0, s[0], dp[0], pb[0], ds[0]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         // segment C: dV, dK of block 0 under the VALU of block 1
-        pv_rows<C>(dv, gt, voff, pb[0]);
-        pv_rows<C>(dk, qt, voff, ds[0]);
+        pv_rows2<C>(dv, gt, pb[0], dk, qt, ds[0], voff);
         elementwise(mk, t, st, 1, s[1], dp[1], pb[1], ds[1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);
         }
         __builtin_amdgcn_sched_barrier(0);
         // segment D: dV, dK of block 1
-        pv_rows<C>(dv, gt + 32 * C::RB, voff, pb[1]);
-        pv_rows<C>(dk, qt + 32 * C::RB, voff, ds[1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
-        }
+        pv_rows2<C>(dv, gt + 32 * C::RB, pb[1], dk, qt + 32 * C::RB, ds[1], voff);
     };
     auto sync_issue = [&](int t) {
         wait_vm();
