@@ -164,6 +164,72 @@ __device__ __forceinline__ void pv_rows2(f32x16 (&o1)[C::DB], const char *blk1,
         }
 }
 
+// S = K-tile rows x qf and dP = V-tile rows x gf for both 32-key blocks, with
+// a rolling window of L operand reads ahead of the MFMAs.  Each step (MFMA i,
+// then the read for MFMA i + L) is a scheduling region of its own, so the
+// scheduler cannot pull the reads back next to their MFMAs.
+template <class C, int L>
+__device__ __forceinline__ void qk_dq_rolling(f32x16 (&s)[C::KB], f32x16 (&dp)[C::KB], const char *Ks,
+                                              const char *Vs, int koffk, int koffv,
+                                              const typename Mma16<typename C::T>::v8 (&qf)[C::KS],
+                                              const typename Mma16<typename C::T>::v8 (&gf)[C::KS]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+    constexpr int N = 2 * C::KB * C::KS;
+    asm volatile("" : "+v"(koffk), "+v"(koffv));
+    auto rd = [&](int i) {
+        const int ks = i / (2 * C::KB), kb = (i >> 1) % C::KB, wh = i & 1;
+        const char *base = (wh ? Vs : Ks) + kb * 32 * C::RB;
+        return *(const v8 *)(base + (((wh ? koffv : koffk) ^ (32 * (ks & 7))) + 256 * (ks >> 3)));
+    };
+    v8 buf[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) buf[j] = rd(j);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+        s[kb] = (f32x16){};
+        dp[kb] = (f32x16){};
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int ks = i / (2 * C::KB), kb = (i >> 1) % C::KB, wh = i & 1;
+        const v8 a = buf[i % L];
+        if (wh)
+            dp[kb] = M::mma(a, gf[ks], dp[kb]);
+        else
+            s[kb] = M::mma(a, qf[ks], s[kb]);
+        if (i + L < N) buf[i % L] = rd(i + L);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// o^T += V_tile^T P^T as pv_tile, with a rolling window of L MFMAs' operand
+// reads (two transposed reads each) ahead.
+template <class C, int L>
+__device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs, const int (&voff)[C::NVO],
+                                              const typename Mma16<typename C::T>::v8 (&pb)[C::KB][2]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+    constexpr int N = C::KB * 2 * C::DB;
+    auto rd = [&](int i) {
+        const int kb = i / (2 * C::DB), k2 = (i / C::DB) & 1, db = i % C::DB;
+        const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + voff[db & 3] + 256 * (db >> 2);
+        const i16x4 lo = lds_read_tr16(base);
+        const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+        return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    v8 buf[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) buf[j] = rd(j);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int kb = i / (2 * C::DB), k2 = (i / C::DB) & 1, db = i % C::DB;
+        o[db] = M::mma(buf[i % L], pb[kb][k2], o[db]);
+        if (i + L < N) buf[i % L] = rd(i + L);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // D_i = sum_c dO_ic O_ic (float32), D/8 lanes per row, 8 elements each.
 template <typename T, int D>
@@ -258,8 +324,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         }
         if (t >= wn) return;
         f32x16 s[C::KB], dp[C::KB];
-        qk_tile<C>(s, kbuf(PAR), koff_k, qf);
-        qk_tile<C>(dp, vbuf(PAR), koff_v, gf);
+        // reads ahead: as many as the register budget of two waves per SIMD allows
+        constexpr int LQ = C::DROP && C::D >= 128 ? 4 : 6;
+        qk_dq_rolling<C, LQ>(s, dp, kbuf(PAR), vbuf(PAR), koff_k, koff_v, qf, gf);
         // keys past n_kv, and (causal) keys after qi, have P = 0
         const bool masked = (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
         const int lim = C::CAUSAL ? min(n_kv, qi + 1) : n_kv;
@@ -292,7 +359,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
                 }
                 ds[kb][k2] = x;
             }
-        pv_tile<C>(dq, kbuf(PAR), voff, ds);
+        pv_dq_rolling<C, 4>(dq, kbuf(PAR), voff, ds);
     };
     for (int t = 0; t < ntile; t += 2) {
         tile(std::integral_constant<int, 0>(), t);
