@@ -260,9 +260,14 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     typedef typename C::T T;
     typedef Mma16<T> M;
     typedef typename M::v8 v8;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-    auto kbuf = [&](int i) { return smem + i * C::TILE; };
-    auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
+    // four LDS objects (K, V x two buffers): a read of one is then not held
+    // up by a copy in flight into another
+    __shared__ __attribute__((aligned(1024))) char sk0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sk1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sv0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sv1[C::TILE];
+    auto kbuf = [&](int i) { return i ? sk1 : sk0; };
+    auto vbuf = [&](int i) { return i ? sv1 : sv0; };
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -379,10 +384,18 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     typedef typename C::T T;
     typedef Mma16<T> M;
     typedef typename M::v8 v8;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-    auto qbuf = [&](int i) { return smem + i * C::TILE; };
-    auto gbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
-    auto sbuf = [&](int i) { return smem + 4 * C::TILE + i * 512; };
+    // separate LDS objects per stream and buffer, so that reads of one buffer
+    // are not held up by the copies in flight into the other (the unmasked
+    // loop below picks every buffer at compile time)
+    __shared__ __attribute__((aligned(1024))) char sq0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sq1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sg0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sg1[C::TILE];
+    __shared__ __attribute__((aligned(16))) char ss0[512];
+    __shared__ __attribute__((aligned(16))) char ss1[512];
+    auto qbuf = [&](int i) { return i ? sq1 : sq0; };
+    auto gbuf = [&](int i) { return i ? sg1 : sg0; };
+    auto sbuf = [&](int i) { return i ? ss1 : ss0; };
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -485,11 +498,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     // scheduling segments: S, dP of block 0; S, dP of block 1 under the VALU
     // of block 0; dV, dK of block 0 under the VALU of block 1; dV, dK of
     // block 1.
-    auto body = [&](auto mk, int t) {
-        const int cur = t & 1;
-        const char *qt = qbuf(cur);
-        const char *gt = gbuf(cur);
-        const float *st = (const float *)sbuf(cur);
+    auto body = [&](auto mk, int t, const char *qt, const char *gt, const char *sb) {
+        const float *st = (const float *)sb;
         f32x16 s[2], dp[2];
         v8 pb[2][2], ds[2][2];
         constexpr int NQK = 2 * C::KS, NPV = 4 * C::DB;  // MFMAs of two products, per block
@@ -537,23 +547,41 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
     };
+    // tile t with its buffers chosen at run time
+    auto tile_rt = [&](auto mk, int t) {
+        sync_issue(t);
+        const int b = t & 1;
+        body(mk, t, qbuf(b), gbuf(b), sbuf(b));
+        pin();
+    };
+    // tile t of parity PAR, buffers fixed
+    auto tile_ct = [&](auto par, int t) {
+        constexpr int PAR = decltype(par)::value;
+        wait_vm();
+        __syncthreads();
+        if (t + 1 < ntile) {
+            plan.issue(qh, (t + 1) * C::BC, n_q, PAR ? sq0 : sq1, w, lane);
+            plan.issue(gh, (t + 1) * C::BC, n_q, PAR ? sg0 : sg1, w, lane);
+            issue_stats(t + 1, PAR ? ss0 : ss1);
+        }
+        body(std::integral_constant<bool, false>(), t, PAR ? sq1 : sq0, PAR ? sg1 : sg0, PAR ? ss1 : ss0);
+        pin();
+    };
     int t = t0;
     for (; t < wt0; ++t) sync_issue(t);
-    for (; t < tm; ++t) {
-        sync_issue(t);
-        body(std::integral_constant<bool, true>(), t);
-        pin();
+    for (; t < tm; ++t) tile_rt(std::integral_constant<bool, true>(), t);
+    if constexpr (C::DROP) {
+        // (one body: the dropout bodies do not fit four copies in registers)
+        for (; t < tf; ++t) tile_rt(std::integral_constant<bool, false>(), t);
+    } else {
+        if (t < tf && (t & 1)) tile_rt(std::integral_constant<bool, false>(), t++);
+        for (; t + 1 < tf; t += 2) {
+            tile_ct(std::integral_constant<int, 0>(), t);
+            tile_ct(std::integral_constant<int, 1>(), t + 1);
+        }
+        if (t < tf) tile_rt(std::integral_constant<bool, false>(), t++);
     }
-    for (; t < tf; ++t) {
-        sync_issue(t);
-        body(std::integral_constant<bool, false>(), t);
-        pin();
-    }
-    for (; t < ntile; ++t) {
-        sync_issue(t);
-        body(std::integral_constant<bool, true>(), t);
-        pin();
-    }
+    for (; t < ntile; ++t) tile_rt(std::integral_constant<bool, true>(), t);
     if (kj < n_kv) {
         const int64_t row = (int64_t)bh * n_kv + kj;
         store_rows<C>(p.dk + row * C::RB, dk, p.scale, h);

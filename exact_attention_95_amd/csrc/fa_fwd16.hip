@@ -177,10 +177,16 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     typedef Mma16<T> M;
     typedef typename M::v8 v8;
     typedef typename M::v4 v4;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-    // LDS: K buffers 0 and 1, then V buffers 0 and 1
-    auto kbuf = [&](int i) { return smem + i * C::TILE; };
-    auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
+    // LDS: K buffers 0 and 1, V buffers 0 and 1, as four separate objects so
+    // that the compiler can tell a read of one buffer from a copy in flight
+    // into another (with one array it waits for every outstanding copy before
+    // each LDS read)
+    __shared__ __attribute__((aligned(1024))) char sk0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sk1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sv0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sv1[C::TILE];
+    auto kbuf = [&](int i) { return i ? sk1 : sk0; };
+    auto vbuf = [&](int i) { return i ? sv1 : sv0; };
 
     const int lane = lane_id();
     const int w = wave_id();
