@@ -160,9 +160,14 @@ __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-    auto kbuf = [&](int i) { return smem + i * C::TILE; };
-    auto vbuf = [&](int i) { return smem + (2 + i) * C::TILE; };
+    // K and V buffers as four LDS objects: a read of one is not held up by a
+    // copy in flight into another
+    __shared__ __attribute__((aligned(1024))) char sk0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sk1[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sv0[C::TILE];
+    __shared__ __attribute__((aligned(1024))) char sv1[C::TILE];
+    auto kbuf = [&](int i) { return i ? sk1 : sk0; };
+    auto vbuf = [&](int i) { return i ? sv1 : sv0; };
 
     const int lane = lane_id();
     const int w = wave_id();
