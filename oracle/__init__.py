@@ -99,7 +99,7 @@ def _declare(lib):
     lib.fa_oracle_attention_dropout.restype = ctypes.c_int
     lib.fa_oracle_attention_dropout.argtypes = [
         _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
-        _u8p, ctypes.c_double, _dp, _dp]
+        _i64p, ctypes.c_int64, _u8p, ctypes.c_double, _dp, _dp]
     lib.fa_oracle_backward_dropout.restype = ctypes.c_int
     lib.fa_oracle_backward_dropout.argtypes = [
         _dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
@@ -335,52 +335,76 @@ def dropout_mask(seed: int, offset: int, bh: int, n_q: int, n_kv: int, p8: int, 
 
 
 def attention_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int,
-                      lib=None):
-    """Attention with dropout in fp64 ([B,H,N,d] or [N,d]); returns (O, LSE)."""
+                      rows=None, lib=None):
+    """Attention with dropout in fp64 ([B,H,N,d] or [N,d]); returns (O, LSE).
+
+    ``rows``: optional flat row indices into B*H*N_q, as in ``attention``; then
+    the results are [len(rows), d] and [len(rows)]."""
     lib = lib or load()
     q4, k4, v4 = (_heads(t) for t in (q, k, v))
     B, H, n_q, d = q4.shape
     n_kv = k4.shape[2]
     p8 = dropout_p8(p, lib)
-    o = np.empty((B, H, n_q, d))
-    lse = np.empty((B, H, n_q))
-    for b in range(B):
-        for h in range(H):
-            keep = dropout_mask(seed, offset, b * H + h, n_q, n_kv, p8, lib)
-            qh, kh, vh = _as_f64(q4[b, h]), _as_f64(k4[b, h]), _as_f64(v4[b, h])
-            oh, lh = np.empty((n_q, d)), np.empty(n_q)
-            st = lib.fa_oracle_attention_dropout(
-                _ptr(qh), _ptr(kh), _ptr(vh), n_q, n_kv, d, float(scale), int(bool(causal)),
-                keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), dropout_rescale(p8), _ptr(oh), _ptr(lh))
-            if st:
-                raise RuntimeError("fa_oracle_attention_dropout failed: %d" % st)
-            o[b, h], lse[b, h] = oh, lh
-    if q.ndim == 2:
-        return o[0, 0], lse[0, 0]
+
+    def head(b, h, local):
+        keep = dropout_mask(seed, offset, b * H + h, n_q, n_kv, p8, lib)
+        qh, kh, vh = _as_f64(q4[b, h]), _as_f64(k4[b, h]), _as_f64(v4[b, h])
+        n_rows = n_q if local is None else local.size
+        oh, lh = np.empty((n_rows, d)), np.empty(n_rows)
+        st = lib.fa_oracle_attention_dropout(
+            _ptr(qh), _ptr(kh), _ptr(vh), n_q, n_kv, d, float(scale), int(bool(causal)),
+            None if local is None else _ptr(local, _i64p), n_rows,
+            keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), dropout_rescale(p8), _ptr(oh), _ptr(lh))
+        if st:
+            raise RuntimeError("fa_oracle_attention_dropout failed: %d" % st)
+        return oh, lh
+
+    if rows is None:
+        o = np.empty((B, H, n_q, d))
+        lse = np.empty((B, H, n_q))
+        for b in range(B):
+            for h in range(H):
+                o[b, h], lse[b, h] = head(b, h, None)
+        if q.ndim == 2:
+            return o[0, 0], lse[0, 0]
+        return o, lse
+    rows = np.asarray(rows, dtype=np.int64).ravel()
+    o = np.empty((rows.size, d))
+    lse = np.empty(rows.size)
+    head_of = rows // n_q
+    for bh in np.unique(head_of):
+        sel = np.nonzero(head_of == bh)[0]
+        b, h = divmod(int(bh), H)
+        o[sel], lse[sel] = head(b, h, np.ascontiguousarray(rows[sel] - bh * n_q))
     return o, lse
 
 
 def backward_dropout(q, k, v, dout, scale: float, causal: bool, p: float, seed: int, offset: int,
-                     lib=None):
-    """Gradients of attention_dropout in fp64; returns (dQ, dK, dV)."""
+                     heads=None, lib=None):
+    """Gradients of attention_dropout in fp64; returns (dQ, dK, dV).
+
+    ``heads``: optional flat (batch, head) indices; then the results are
+    [len(heads), N, d] for those heads only."""
     lib = lib or load()
     q4, k4, v4, g4 = (_heads(t) for t in (q, k, v, dout))
     B, H, n_q, d = q4.shape
     n_kv = k4.shape[2]
     p8 = dropout_p8(p, lib)
-    dq, dk, dv = np.empty((B, H, n_q, d)), np.empty((B, H, n_kv, d)), np.empty((B, H, n_kv, d))
-    for b in range(B):
-        for h in range(H):
-            keep = dropout_mask(seed, offset, b * H + h, n_q, n_kv, p8, lib)
-            qh, kh, vh, gh = (_as_f64(t[b, h]) for t in (q4, k4, v4, g4))
-            a, bk, c = np.empty((n_q, d)), np.empty((n_kv, d)), np.empty((n_kv, d))
-            st = lib.fa_oracle_backward_dropout(
-                _ptr(qh), _ptr(kh), _ptr(vh), _ptr(gh), n_q, n_kv, d, float(scale), int(bool(causal)),
-                keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), dropout_rescale(p8),
-                _ptr(a), _ptr(bk), _ptr(c))
-            if st:
-                raise RuntimeError("fa_oracle_backward_dropout failed: %d" % st)
-            dq[b, h], dk[b, h], dv[b, h] = a, bk, c
+    sel = list(range(B * H)) if heads is None else [int(x) for x in heads]
+    dq, dk, dv = np.empty((len(sel), n_q, d)), np.empty((len(sel), n_kv, d)), np.empty((len(sel), n_kv, d))
+    for n, bh in enumerate(sel):
+        b, h = divmod(bh, H)
+        keep = dropout_mask(seed, offset, bh, n_q, n_kv, p8, lib)
+        qh, kh, vh, gh = (_as_f64(t[b, h]) for t in (q4, k4, v4, g4))
+        st = lib.fa_oracle_backward_dropout(
+            _ptr(qh), _ptr(kh), _ptr(vh), _ptr(gh), n_q, n_kv, d, float(scale), int(bool(causal)),
+            keep.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), dropout_rescale(p8),
+            _ptr(dq[n]), _ptr(dk[n]), _ptr(dv[n]))
+        if st:
+            raise RuntimeError("fa_oracle_backward_dropout failed: %d" % st)
+    if heads is not None:
+        return dq, dk, dv
+    dq, dk, dv = dq.reshape(B, H, n_q, d), dk.reshape(B, H, n_kv, d), dv.reshape(B, H, n_kv, d)
     if q.ndim == 2:
         return dq[0, 0], dk[0, 0], dv[0, 0]
     return dq, dk, dv

@@ -515,13 +515,21 @@ int fa_oracle_dropout_mask(uint64_t seed, uint64_t offset, int64_t bh, int64_t n
  * fa_oracle_naive (three passes over the visible keys), then
  *   O_i = rescale * sum_j P_ij keep_ij v_j,   LSE_i = m_i + ln l_i
  * (the LSE is that of the scores, before dropout).  keep: [n_q, n_kv]
- * bytes; rescale = 1 / (1 - p8 / 256) is passed in.
+ * bytes; rescale = 1 / (1 - p8 / 256) is passed in.  rows: optional
+ * indices of the rows to compute (NULL: all n_q; then n_rows = n_q); row r
+ * of o / lse is query rows[r].
  */
 int fa_oracle_attention_dropout(const double *q, const double *k, const double *v, int64_t n_q,
                                 int64_t n_kv, int64_t d, double scale, int causal,
+                                const int64_t *rows, int64_t n_rows,
                                 const uint8_t *keep, double rescale, double *o, double *lse)
 {
-    if (!q || !k || !v || !keep || !o || !lse || n_q < 0 || n_kv < 1 || d < 1) return 1;
+    if (!q || !k || !v || !keep || !o || !lse || n_q < 0 || n_kv < 1 || d < 1 || n_rows < 0) return 1;
+    if (!rows && n_rows != n_q) return 1;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= n_q) return 1;
+    }
     int status = 0;
 #pragma omp parallel
     {
@@ -531,8 +539,9 @@ int fa_oracle_attention_dropout(const double *q, const double *k, const double *
             status = 2;
         }
 #pragma omp for schedule(dynamic, 4)
-        for (int64_t i = 0; i < n_q; ++i) {
+        for (int64_t r = 0; r < n_rows; ++r) {
             if (!s) continue;
+            const int64_t i = rows ? rows[r] : r;
             const int64_t nv = visible_keys(i, n_kv, causal);
             double m = -INFINITY;
             for (int64_t j = 0; j < nv; ++j) {
@@ -541,14 +550,14 @@ int fa_oracle_attention_dropout(const double *q, const double *k, const double *
             }
             double l = 0.0;
             for (int64_t j = 0; j < nv; ++j) l = l + exp(s[j] - m);
-            double *oi = o + i * d;
+            double *oi = o + r * d;
             for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
             for (int64_t j = 0; j < nv; ++j) {
                 if (!keep[i * n_kv + j]) continue;
                 const double zij = rescale * exp(s[j] - m) / l;
                 for (int64_t c = 0; c < d; ++c) oi[c] += zij * v[j * d + c];
             }
-            lse[i] = m + log(l);
+            lse[r] = m + log(l);
         }
         free(s);
     }

@@ -12,7 +12,7 @@ import torch
 
 from conftest import gpu_available
 from exact_attention_95_amd import fa
-from exact_attention_95_amd.inputs import make_dout, random_problem
+from exact_attention_95_amd.inputs import WORKLOADS, make_dout, make_inputs, random_problem
 import oracle
 from parity import assert_grads_within, assert_within, errors, grad_errors, say
 
@@ -76,3 +76,47 @@ def test_zero_dropout_is_the_plain_kernel_and_seeds_matter():
     assert torch.equal(a, b)                                  # replayable
     assert not torch.equal(a, c)                              # the seed matters
     assert torch.equal(la, l0) and torch.equal(lc, l0)        # LSE is that of the scores
+
+
+@pytest.mark.parametrize("name", ["headline_bf16_n8192_d128", "headline_bf16_causal_n8192_d128"])
+def test_dropout_full_size(name):
+    """Full-size forward and backward with dropout p = 0.1 in the launch
+    configuration the benchmark times: O and LSE on sampled rows of two heads
+    (every boosted row of those heads among them), and dQ, dK, dV of one
+    whole head, against the oracle."""
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    dout = make_dout(w)
+    p = 0.1
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, scale=w.sm_scale, causal=w.causal, dropout_p=p, seed=SEED, offset=OFFSET)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, dout.cuda(), scale=w.sm_scale, causal=w.causal, dropout_p=p,
+                        seed=SEED, offset=OFFSET)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng([w.seed_id, 78])
+    heads = rng.choice(w.B * w.H, size=2, replace=False)
+    rows = []
+    for bh in heads:
+        base = bh * w.n_q
+        rows.append(base + rng.integers(0, w.n_q, 96))
+        rows.append(base + np.array([0, 1, 255, 256, w.n_q - 1]))
+        b = x["boost_rows"]
+        rows.append(b[(b >= base) & (b < base + w.n_q)])
+    rows = np.unique(np.concatenate(rows)).astype(np.int64)
+    idx = torch.from_numpy(rows).cuda()
+    o_s = o.reshape(-1, w.d)[idx].double().cpu().numpy()
+    lse_s = lse.reshape(-1)[idx].double().cpu().numpy()
+    o_ref, lse_ref = oracle.attention_dropout(x["q"], x["k"], x["v"], w.sm_scale, w.causal, p, SEED, OFFSET,
+                                              rows=rows)
+    err = errors(o_s, lse_s, o_ref, lse_ref)
+    say(name, rows.size, "rows", err)
+    assert_within(w, err, name + " dropout fwd")
+    bh = int(heads[0])
+    b, h = divmod(bh, w.H)
+    got = [t[b, h].double().cpu().numpy() for t in (dq, dk, dv)]
+    del dq, dk, dv, o, q, k, v
+    rq, rk, rv = oracle.backward_dropout(x["q"], x["k"], x["v"], dout, w.sm_scale, w.causal, p, SEED, OFFSET,
+                                         heads=[bh])
+    errs = {"dQ": grad_errors(got[0], rq[0]), "dK": grad_errors(got[1], rk[0]), "dV": grad_errors(got[2], rv[0])}
+    say(name, "head", bh, errs)
+    assert_grads_within(errs, name + " dropout bwd")

@@ -117,6 +117,28 @@ def test_dropout_gradients_match_differences(causal):
         assert np.abs(num - got[which]).max() <= 5e-8
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_selections_equal_the_full_result(causal):
+    """Selected rows (attention) and selected heads (gradients) equal the
+    corresponding parts of the whole computation, with the mask of the right
+    slice and row."""
+    rng = np.random.default_rng(7 + causal)
+    B, H, n_q, n_kv, d = 2, 3, 23, 31, 5
+    q, k, v, g = (rng.standard_normal((B, H, n, d)) for n in (n_q, n_kv, n_kv, n_q))
+    args = (0.7, causal, 0.3, 99, 4)
+    o, lse = oracle.attention_dropout(q, k, v, *args)
+    rows = np.array([0, 5, 22, n_q + 3, 2 * n_q + 11, 5 * n_q + 22, 4 * n_q])
+    o_r, lse_r = oracle.attention_dropout(q, k, v, *args, rows=rows)
+    assert np.abs(o_r - o.reshape(-1, d)[rows]).max() <= 1e-15
+    assert np.abs(lse_r - lse.reshape(-1)[rows]).max() <= 1e-15
+    dq, dk, dv = oracle.backward_dropout(q, k, v, g, *args)
+    heads = [4, 1]
+    sq, sk, sv = oracle.backward_dropout(q, k, v, g, *args, heads=heads)
+    for n, bh in enumerate(heads):
+        b, h = divmod(bh, H)
+        assert np.array_equal(sq[n], dq[b, h]) and np.array_equal(sk[n], dk[b, h]) and np.array_equal(sv[n], dv[b, h])
+
+
 def test_dropout_gradients_without_dropout_equal_plain():
     rng = np.random.default_rng(5)
     q, k, v, g = (rng.standard_normal(s) for s in ((7, 5), (11, 5), (11, 5), (7, 5)))
