@@ -557,7 +557,7 @@ int fa_oracle_attention_dropout(const double *q, const double *k, const double *
                 const double zij = rescale * exp(s[j] - m) / l;
                 for (int64_t c = 0; c < d; ++c) oi[c] += zij * v[j * d + c];
             }
-            lse[r] = m + log(l);
+            lse[r] = log(l) + m;
         }
         free(s);
     }
