@@ -145,8 +145,8 @@ int fa_validate(const fa_fwd_args *args);
  * the rule of "FlashAttention 与显存" plate 08 applied to whole chunks,
  * L = ln sum_s exp(L_s), O = sum_s exp(L_s - L) O_s, and writes O and LSE as
  * fa_fwd_ex does.  The result equals fa_fwd_ex's up to rounding; it pays off
- * when B * H * ceil(N_q / 128) workgroups cannot fill the GPU (few query rows,
- * long key ranges).
+ * when fa_fwd_ex's workgroups (B * H * ceil(N_q / 256) at d = 128) cannot fill
+ * the GPU (few query rows, long key ranges).
  *
  * args: as for fa_fwd_ex; dtype FA_BF16 or FA_F16 and d in {64, 128}
  * (otherwise FA_ERR_VARIANT); tile_override 0 or 1.  num_splits: 0 lets the
@@ -257,7 +257,8 @@ int fa_num_variants(int dtype, int64_t d, int causal);
 
 /*
  * Static description of variant v (1-based) for (dtype, d, causal), e.g.
- * "br256_bc64_w8"; "" if v is out of range.  Host-only, no HIP call.
+ * "br8x32_bc64" (8 waves of 32 query rows, 64-key tiles); "" if v is out of
+ * range.  Host-only, no HIP call.
  */
 const char *fa_variant_name(int dtype, int64_t d, int causal, int v);
 
