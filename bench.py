@@ -197,6 +197,74 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str, bwd: bool 
     return rec
 
 
+def launch_stats(step, stream, n: int, flush=None) -> dict:
+    """Per-launch durations (ms) of n launches, each bracketed by HIP events on
+    the launch stream; with flush, a device buffer is overwritten before every
+    launch so that the launch starts with cold caches (L2 and the 256 MB
+    Infinity Cache)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i, (a, b) in enumerate(evs):
+            if flush is not None:
+                flush.fill_(i & 0x7F)
+            a.record(stream)
+            step()
+            b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"median": round(float(np.median(ms)), 4), "min": round(ms[0], 4),
+            "max": round(ms[-1], 4), "launches": n}
+
+
+# matrix-core FLOPs per clock and CU (the published peak / (256 CUs x 2.4 GHz))
+MFMA_FLOP_PER_CLK_CU = {"bf16": 4096, "f16": 4096, "fp8_e4m3": 8192, "f32": 256}
+
+
+def device_probe(dtype: str, stream) -> dict:
+    """Rates measured on this device by the library's probe kernels: the
+    sustained MFMA rate of the workload's input type, v_exp_f32 and fp32 FMA
+    throughput, and the shader clock while each ran (cycle counter against
+    the constant wall clock)."""
+    import torch
+    from exact_attention_95_amd import fa
+    kind_of = {"bf16": fa.FA_PROBE_MFMA_BF16, "f16": fa.FA_PROBE_MFMA_F16,
+               "fp8_e4m3": fa.FA_PROBE_MFMA_FP8, "f32": fa.FA_PROBE_MFMA_F32}
+    khz = fa.fa_probe_wall_clock_khz()
+
+    def run(kind, n_wg, iters):
+        sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+        clocks = torch.zeros(n_wg * 8, dtype=torch.int64, device="cuda")
+        for it in (max(1, iters // 16), iters):  # warm-up, then the timed launch
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            st = fa.fa_probe(kind, n_wg, it, sink.data_ptr(), clocks.data_ptr(), stream.cuda_stream)
+            ev1.record(stream)
+            if st != fa.FA_OK:
+                raise fa.FaError(st)
+            torch.cuda.synchronize()
+        sec = ev0.elapsed_time(ev1) * 1e-3
+        work = n_wg * 4 * iters * fa.fa_probe_work_per_iter(kind)
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = float(np.median(c[:, 0] / c[:, 1])) * khz * 1e-6 if khz > 0 else None
+        return work / sec, ghz
+
+    # 2 waves per SIMD for the MFMA loop, 8 for the VALU loops
+    rate, ghz = run(kind_of[dtype], 512, {"fp8_e4m3": 32768, "f32": 32768}.get(dtype, 65536))
+    exp_rate, exp_ghz = run(fa.FA_PROBE_EXP, 2048, 16384)
+    fma_rate, fma_ghz = run(fa.FA_PROBE_FMA, 2048, 65536)
+    per_clk = lambda r, g: round(r / (256 * g * 1e9), 2) if g else None
+    return {
+        "mfma_tflops": round(rate / 1e12, 1), "mfma_dtype": dtype,
+        "clock_ghz_during_mfma": round(ghz, 3) if ghz else None,
+        "mfma_flop_per_clk_cu": per_clk(rate, ghz),
+        "mfma_flop_per_clk_cu_published": MFMA_FLOP_PER_CLK_CU[dtype],
+        "exp_per_clk_cu": per_clk(exp_rate, exp_ghz), "clock_ghz_during_exp": exp_ghz and round(exp_ghz, 3),
+        "fma_per_clk_cu": per_clk(fma_rate, fma_ghz), "clock_ghz_during_fma": fma_ghz and round(fma_ghz, 3),
+    }
+
+
 def memory_report(names) -> list:
     """Device memory of fa_fwd (inputs, outputs and nothing else) against the
     analytic footprint of materialising S and P (N x N each, input dtype)."""
@@ -246,6 +314,9 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.json from two rocprofv3 --pmc "
                          "counter_collection.csv files and exit")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-launch (warm and cold-cache) timings and the device "
+                         "probes that follow the timed region (for profiler runs)")
     ap.add_argument("--memory-report", action="store_true",
                     help="print device memory of the long causal fp16 workloads vs a "
                          "materialised N x N baseline and exit")
@@ -348,6 +419,17 @@ def main(argv=None) -> int:
         print("non-finite output", file=sys.stderr)
         return 1
 
+    extras = {}
+    if not args.no_extras:
+        # per-launch spread, warm and with cold caches (512 MB written between
+        # launches), then the device's own rates; all after the timed region
+        extras["launch_ms"] = {"warm": launch_stats(step, stream, args.steps)}
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        extras["launch_ms"]["cold"] = launch_stats(step, stream, args.steps, flush)
+        extras["launch_ms"]["cold"]["flush_bytes"] = flush.numel()
+        del flush
+        extras["device"] = device_probe(w.dtype, stream)
+
     if args.copy_calibration:
         # a plain device-to-device copy of exactly 1 GiB (hipMemcpy's copy kernel)
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -393,6 +475,12 @@ def main(argv=None) -> int:
                      "traffic": stored_traffic(w.name, w.dtype, args.bwd),
                      "kernel_ms": round(kernel_ms, 4)},
     }
+    if extras:
+        rec.update(extras)
+        if not hbm_bound:
+            # the kernel's rate against the MFMA rate measured on this device
+            rec["roofline"]["frac_of_measured_peak"] = round(
+                achieved / extras["device"]["mfma_tflops"], 4)
     if not args.no_cpu_baseline and args.dropout == 0.0:
         rec["cpu_baseline"] = (cpu_baseline_bwd(w, x, do.cpu()) if args.bwd else cpu_baseline(w, x))
     print(json.dumps(rec), flush=True)

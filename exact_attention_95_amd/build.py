@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_fwd8.hip", "fa_bwd16.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_fwd8.hip", "fa_bwd16.hip", "fa_probe.hip"]
 ARCH = "gfx950"
 
 COMMON = [

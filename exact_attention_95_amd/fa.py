@@ -2,10 +2,12 @@
 
 The functions ``fa_fwd``, ``fa_fwd_ex``, ``fa_validate``, ``fa_strerror``,
 ``fa_num_variants``, ``fa_variant_name``, ``fa_fwd_splitkv``,
-``fa_splitkv_workspace_bytes``, ``fa_bwd``, ``fa_bwd_validate`` and
-``fa_bwd_workspace_bytes`` mirror the C entry points of the same names.  ``fwd`` is the torch convenience form: it allocates O and LSE
-with torch on the inputs' device and calls ``fa_fwd_ex`` on torch's current
-stream.  All attention arithmetic runs in the HIP kernels; there is no CPU
+``fa_splitkv_workspace_bytes``, ``fa_bwd``, ``fa_bwd_validate``,
+``fa_bwd_workspace_bytes``, ``fa_dropout_mask`` and the measurement probes
+``fa_probe``, ``fa_probe_work_per_iter`` and ``fa_probe_wall_clock_khz``
+(include/fa_probe.h) mirror the C entry points of the same names.  ``fwd``
+is the torch convenience form: it allocates O and LSE with torch on the
+inputs' device and calls ``fa_fwd_ex`` on torch's current stream.  All attention arithmetic runs in the HIP kernels; there is no CPU
 path, and the library must have been built (``exact_attention_95_amd.build``).
 """
 from __future__ import annotations
@@ -24,6 +26,10 @@ FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
             "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_bwd",
             "fa_bwd_validate", "fa_bwd_workspace_bytes", "fa_dropout_mask")
+# measurement probes (include/fa_probe.h)
+PROBE_EXPORTED = ("fa_probe", "fa_probe_work_per_iter", "fa_probe_wall_clock_khz")
+(FA_PROBE_MFMA_BF16, FA_PROBE_MFMA_F16, FA_PROBE_MFMA_FP8, FA_PROBE_MFMA_F32, FA_PROBE_EXP,
+ FA_PROBE_FMA) = range(6)
 
 
 class FaFwdArgs(ctypes.Structure):
@@ -105,6 +111,12 @@ def load(path: str = LIB_PATH):
             lib.fa_dropout_mask.restype = ctypes.c_int
             lib.fa_dropout_mask.argtypes = [ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64, i64, i64,
                                             i64, vp, vp]
+            lib.fa_probe.restype = ctypes.c_int
+            lib.fa_probe.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+            lib.fa_probe_work_per_iter.restype = ctypes.c_double
+            lib.fa_probe_work_per_iter.argtypes = [ctypes.c_int]
+            lib.fa_probe_wall_clock_khz.restype = i64
+            lib.fa_probe_wall_clock_khz.argtypes = []
             _lib = lib
         return _lib
 
@@ -157,6 +169,18 @@ def fa_bwd_workspace_bytes(args: FaBwdArgs) -> int:
 def fa_dropout_mask(dropout_p, seed, offset, BH, N_q, N_kv, mask, stream=None) -> int:
     return load().fa_dropout_mask(float(dropout_p), int(seed) & (2**64 - 1), int(offset) & (2**64 - 1),
                                   BH, N_q, N_kv, mask, stream)
+
+
+def fa_probe(kind, n_wg, iters, sink, clocks=None, stream=None) -> int:
+    return load().fa_probe(kind, n_wg, iters, sink, clocks, stream)
+
+
+def fa_probe_work_per_iter(kind) -> float:
+    return load().fa_probe_work_per_iter(kind)
+
+
+def fa_probe_wall_clock_khz() -> int:
+    return load().fa_probe_wall_clock_khz()
 
 
 def _dtype_code(t) -> int:

@@ -1,5 +1,6 @@
 """C-ABI tests that need no GPU: the library loads, exports every function
-include/fa.h declares, and fa_validate reaches every pre-launch status."""
+include/fa.h and include/fa_probe.h declare, and fa_validate reaches every
+pre-launch status."""
 import ctypes
 import math
 import os
@@ -10,24 +11,46 @@ import pytest
 from exact_attention_95_amd import fa
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "fa_probe.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
+    probes = declared_functions(PROBE_HEADER)
     assert set(names) == set(fa.EXPORTED)
+    assert set(probes) == set(fa.PROBE_EXPORTED)
     lib = fa.load()
-    for n in names:
+    for n in names + probes:
         assert hasattr(lib, n), n
     # and nothing but these fa_ symbols is exported as a C function
     out = os.popen("nm -D --defined-only %s" % fa.LIB_PATH).read()
     exported = {m for m in re.findall(r" T (fa_\w+)$", out, flags=re.M)}
-    assert exported == set(names)
+    assert exported == set(names) | set(probes)
+
+
+def test_probe_host_side():
+    """Work per loop iteration of each probe, and the argument checks that run
+    before any HIP call."""
+    mfma = {fa.FA_PROBE_MFMA_BF16: 32 * 32 * 16, fa.FA_PROBE_MFMA_F16: 32 * 32 * 16,
+            fa.FA_PROBE_MFMA_FP8: 32 * 32 * 64, fa.FA_PROBE_MFMA_F32: 32 * 32 * 2}
+    for kind, macs in mfma.items():
+        assert fa.fa_probe_work_per_iter(kind) == 8 * 2 * macs  # 8 MFMAs per iteration
+    assert fa.fa_probe_work_per_iter(fa.FA_PROBE_EXP) == 16 * 64
+    assert fa.fa_probe_work_per_iter(fa.FA_PROBE_FMA) == 16 * 64
+    assert fa.fa_probe_work_per_iter(6) == 0.0
+    assert fa.fa_probe(6, 1, 1, 0x1000) == fa.FA_ERR_DTYPE
+    assert fa.fa_probe(-1, 1, 1, 0x1000) == fa.FA_ERR_DTYPE
+    assert fa.fa_probe(fa.FA_PROBE_EXP, 0, 1, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe(fa.FA_PROBE_EXP, (1 << 20) + 1, 1, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 0, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe(fa.FA_PROBE_EXP, 1, (1 << 30) + 1, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, None) == fa.FA_ERR_NULL
 
 
 def test_args_struct_layout(tmp_path):
