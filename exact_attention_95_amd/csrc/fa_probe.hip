@@ -165,6 +165,7 @@ extern "C" int fa_probe(int kind, int64_t n_wg, int64_t iters, float *sink, uint
     if (kind < FA_PROBE_MFMA_BF16 || kind > FA_PROBE_FMA) return FA_ERR_DTYPE;
     if (n_wg < 1 || n_wg > (1 << 20) || iters < 1 || iters > (1 << 30)) return FA_ERR_SHAPE;
     if (!sink) return FA_ERR_NULL;
+    if ((uintptr_t)sink % alignof(float) || (uintptr_t)clocks % alignof(uint64_t)) return FA_ERR_ALIGN;
     if (!on_gfx950()) return FA_ERR_DEVICE;
     const dim3 grid((unsigned)n_wg), block(kThreads);
     hipStream_t s = (hipStream_t)stream;

@@ -21,7 +21,8 @@
  * asynchronous on stream (hipStream_t, NULL = null stream).
  *
  * Errors.  0 (FA_OK); FA_ERR_SHAPE for n_wg outside [1, 2^20] or iters outside
- * [1, 2^30]; FA_ERR_NULL for a NULL sink; FA_ERR_DTYPE for an unknown kind;
+ * [1, 2^30]; FA_ERR_NULL for a NULL sink; FA_ERR_ALIGN for a sink not 4-byte
+ * or clocks not 8-byte aligned; FA_ERR_DTYPE for an unknown kind;
  * FA_ERR_DEVICE without a gfx950 device; FA_ERR_LAUNCH if the launch fails.
  */
 #ifndef FA_PROBE_H_

@@ -51,6 +51,8 @@ def test_probe_host_side():
     assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 0, 0x1000) == fa.FA_ERR_SHAPE
     assert fa.fa_probe(fa.FA_PROBE_EXP, 1, (1 << 30) + 1, 0x1000) == fa.FA_ERR_SHAPE
     assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, None) == fa.FA_ERR_NULL
+    assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, 0x1002) == fa.FA_ERR_ALIGN
+    assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, 0x1000, 0x2004) == fa.FA_ERR_ALIGN
 
 
 def test_args_struct_layout(tmp_path):
