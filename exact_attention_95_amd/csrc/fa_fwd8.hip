@@ -8,11 +8,13 @@
 //
 //   S^T = K Q^T        E4M3 codes; the descales of Q and K are folded into
 //                      the exponent factor c = |scale| dq dk log2(e)
-//   P = exp2(S c - m)  float32; the reference max follows every increase
-//                      (so P <= 1); the row sum l accumulates the float32 P
-//   O^T += V^T (256 P)^T  P scaled by 2^8 into E4M3's normal range and
-//                      rounded to E4M3; V read with ds_read_b64_tr_b8
-//   O = O_acc dv / (256 l)   stored as bfloat16
+//   P' = exp2(S c - m + 8) = 256 P   float32; the reference max follows every
+//                      increase (so P <= 1); 2^8 scales P into E4M3's normal
+//                      range and is folded into the exponent; the row sum l
+//                      accumulates the float32 P'
+//   O^T += V^T P'^T    P' rounded to E4M3; V read with ds_read_b64_tr_b8
+//   O = O_acc dv / l   stored as bfloat16 (the 2^8 cancels);
+//   LSE = (m - 8 + log2 l) ln 2
 //
 // Key order inside a 32-key block: row rho of the S^T MFMA is key
 // pi(rho) = 16 ((rho/4) % 2) + 4 (rho/8) + rho % 4, which makes the S^T
@@ -120,9 +122,10 @@ __device__ __forceinline__ void mask8(f32x16 (&s)[C::KB], int t0, int qi, int n_
 }
 
 // Online-softmax step (plate 08 merge): the reference max follows every
-// increase of the row max, P = exp2(S c - m) <= 1, the float32 P is summed
-// into l_acc and 256 P is rounded to E4M3 into the P^T operand; `raised` and
-// alpha tell the caller to rescale O before accumulating this tile.
+// increase of the row max, so P = exp2(S c - m) <= 1; the kernel computes
+// P' = 256 P = exp2(S c - m + 8) directly, sums the float32 P' into l_acc and
+// rounds P' to E4M3 into the P^T operand; `raised` and alpha tell the caller
+// to rescale O before accumulating this tile.
 template <class C>
 __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m_use, float &l_acc,
                                          float &alpha, bool &raised, float c) {
@@ -139,7 +142,7 @@ __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m
     alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
     l_acc *= alpha;
     m_use = m_new;
-    const float mref = (m_use == kNegInf) ? 0.f : m_use;
+    const float bias = 8.f - ((m_use == kNegInf) ? 0.f : m_use);
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -148,11 +151,11 @@ __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w4 + e], c, -mref));
+                v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w4 + e], c, bias));
                 l4[e] += v[e];
             }
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(256.f * v[0], 256.f * v[1], 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(256.f * v[2], 256.f * v[3], word, true);
+            int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+            word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
             pb[4 * kb + w4] = word;
         }
     l_acc += (l4[0] + l4[1]) + (l4[2] + l4[3]);
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
     both_halves8(l_acc, lo, hi);
     const float l_tot = lo + hi;
     if (qi >= n_q) return;
-    const float inv = p.o_mul / (256.f * l_tot);
+    const float inv = p.o_mul / l_tot;
     char *orow = p.o + ((int64_t)bh * n_q + qi) * (2 * C::D);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
             for (int e = 0; e < 4; ++e) out[e] = (__bf16)(o[db][4 * jj + e] * inv);
             *(bf16x4 *)(orow + 2 * (32 * db + 8 * jj + 4 * h)) = out;
         }
-    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
+    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use - 8.f + __log2f(l_tot)) * kLn2;
 }
 
 template <class C>
