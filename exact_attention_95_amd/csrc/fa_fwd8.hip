@@ -8,13 +8,15 @@
 //
 //   S^T = K Q^T        E4M3 codes; the descales of Q and K are folded into
 //                      the exponent factor c = |scale| dq dk log2(e)
-//   P' = exp2(S c - m + 8) = 256 P   float32; the reference max follows every
-//                      increase (so P <= 1); 2^8 scales P into E4M3's normal
+//   P' = exp2(S c - m + 6) = 64 P   float32; the reference max m is raised
+//                      only when the tile max exceeds it by more than 2 (log2
+//                      units), so P <= 4 and P' <= 256 < 448 (E4M3's largest
+//                      value); the factor 2^6 scales P into E4M3's normal
 //                      range and is folded into the exponent; the row sum l
 //                      accumulates the float32 P'
 //   O^T += V^T P'^T    P' rounded to E4M3; V read with ds_read_b64_tr_b8
-//   O = O_acc dv / l   stored as bfloat16 (the 2^8 cancels);
-//   LSE = (m - 8 + log2 l) ln 2
+//   O = O_acc dv / l   stored as bfloat16 (the 2^6 cancels);
+//   LSE = (m - 6 + log2 l) ln 2
 //
 // Key order inside a 32-key block: row rho of the S^T MFMA is key
 // pi(rho) = 16 ((rho/4) % 2) + 4 (rho/8) + rho % 4, which makes the S^T
@@ -38,6 +40,10 @@ struct Cfg8 {
     static constexpr int KS = D / 64;       // k-steps of S^T = K Q^T
     static constexpr int KB = BC / 32;
     static constexpr int DB = D / 32;
+    // reference max raised only past TAU (log2 units), so P <= 2^TAU; P is
+    // stored as 2^PSHIFT P, at most 2^(TAU + PSHIFT) = 256 < 448 (E4M3's max)
+    static constexpr float TAU = 2.0f, PSHIFT = 6.0f;
+    static_assert(TAU + PSHIFT <= 8.0f, "scaled P must stay below E4M3's largest value");
     static_assert(TILE == 1024 * NW, "one copy instruction per wave per tile");
 };
 
@@ -121,11 +127,12 @@ __device__ __forceinline__ void mask8(f32x16 (&s)[C::KB], int t0, int qi, int n_
         }
 }
 
-// Online-softmax step (plate 08 merge): the reference max follows every
-// increase of the row max, so P = exp2(S c - m) <= 1; the kernel computes
-// P' = 256 P = exp2(S c - m + 8) directly, sums the float32 P' into l_acc and
-// rounds P' to E4M3 into the P^T operand; `raised` and alpha tell the caller
-// to rescale O before accumulating this tile.
+// Online-softmax step (plate 08 merge): the reference max is raised when the
+// tile's row max exceeds it by more than TAU (wave-uniform decision), so
+// P = exp2(S c - m) <= 2^TAU; the kernel computes P' = 2^PSHIFT P =
+// exp2(S c - m + PSHIFT) directly, sums the float32 P' into l_acc and rounds
+// P' to E4M3 into the P^T operand; `raised` and alpha tell the caller to
+// rescale O before accumulating this tile.
 template <class C>
 __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m_use, float &l_acc,
                                          float &alpha, bool &raised, float c) {
@@ -137,12 +144,12 @@ __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m
     float lo, hi;
     both_halves8(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])), lo, hi);
     const float mt = fmaxf(lo, hi) * c;
-    raised = __any(mt > m_use);
+    raised = __any(mt > m_use + C::TAU);
     const float m_new = raised ? fmaxf(m_use, mt) : m_use;
     alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
     l_acc *= alpha;
     m_use = m_new;
-    const float bias = 8.f - ((m_use == kNegInf) ? 0.f : m_use);
+    const float bias = C::PSHIFT - ((m_use == kNegInf) ? 0.f : m_use);
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
             for (int e = 0; e < 4; ++e) out[e] = (__bf16)(o[db][4 * jj + e] * inv);
             *(bf16x4 *)(orow + 2 * (32 * db + 8 * jj + 4 * h)) = out;
         }
-    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use - 8.f + __log2f(l_tot)) * kLn2;
+    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use - C::PSHIFT + __log2f(l_tot)) * kLn2;
 }
 
 template <class C>
