@@ -319,8 +319,11 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) dq[db] = (f32x16){};
 
-    auto tile = [&](auto par, int t) {
+    // MASKED: the tile holds keys past n_kv or (causal) keys after some row
+    // of this wave; only such tiles carry the compare and select per element
+    auto tile = [&](auto par, auto msk, int t) {
         constexpr int PAR = decltype(par)::value;
+        constexpr bool MASKED = decltype(msk)::value;
         wait_vm();
         __syncthreads();
         if (t + 1 < ntile) {
@@ -333,7 +336,6 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         constexpr int LQ = C::DROP && C::D >= 128 ? 4 : 6;
         qk_dq_rolling<C, LQ>(s, dp, kbuf(PAR), vbuf(PAR), koff_k, koff_v, qf, gf);
         // keys past n_kv, and (causal) keys after qi, have P = 0
-        const bool masked = (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
         const int lim = C::CAUSAL ? min(n_kv, qi + 1) : n_kv;
         v8 ds[C::KB][2];
         // dropout keep bits: keys t BC + 32 kb + 16 k2 + 8 half + 4 h + (0..3)
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
                 for (int e = 0; e < 8; ++e) {
                     const int r = 8 * k2 + e;
                     float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -lse2));
-                    if (masked) {
+                    if constexpr (MASKED) {
                         const int key = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                         pr = key < lim ? pr : 0.f;
                     }
@@ -366,10 +368,29 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
             }
         pv_dq_rolling<C, 4>(dq, kbuf(PAR), voff, ds);
     };
-    for (int t = 0; t < ntile; t += 2) {
-        tile(std::integral_constant<int, 0>(), t);
-        if (t + 1 >= ntile) break;
-        tile(std::integral_constant<int, 1>(), t + 1);
+    // Tiles [0, tu) need no mask for any row of this wave (all keys below n_kv
+    // and, causal, at most the wave's first row); they run in pairs with
+    // compile-time buffers and no per-element compare.  The rest run with the
+    // mask.  Every wave passes one barrier per tile either way.  With dropout
+    // every tile takes the masked body (a second body would spill).
+    const std::integral_constant<int, 0> p0;
+    const std::integral_constant<int, 1> p1;
+    const std::false_type full;
+    const std::true_type part;
+    int tu = C::DROP ? 0 : n_kv / C::BC;
+    if (C::CAUSAL) tu = min(tu, (wq0 + 1) / C::BC);
+    int t = 0;
+    if constexpr (!C::DROP) {
+        for (; t + 2 <= tu; t += 2) {
+            tile(p0, full, t);
+            tile(p1, full, t + 1);
+        }
+    }
+    for (; t < ntile; ++t) {
+        if (t & 1)
+            tile(p1, part, t);
+        else
+            tile(p0, part, t);
     }
     if (qi < n_q) store_rows<C>(p.dq + ((int64_t)bh * n_q + qi) * C::RB, dq, p.scale, h);
 }
