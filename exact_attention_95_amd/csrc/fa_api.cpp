@@ -394,7 +394,7 @@ extern "C" int fa_bwd_validate(const fa_bwd_args *a) {
 
 extern "C" int64_t fa_bwd_workspace_bytes(const fa_bwd_args *a) {
     if (fa_bwd_validate(a) != FA_OK) return -1;
-    return align256(a->B * a->H * a->N_q * 4);
+    return 2 * align256(a->B * a->H * a->N_q * 4);  // D, then LSE log2(e)
 }
 
 extern "C" int fa_bwd(const fa_bwd_args *a, void *workspace, int64_t workspace_bytes) {
@@ -426,6 +426,7 @@ extern "C" int fa_bwd(const fa_bwd_args *a, void *workspace, int64_t workspace_b
     p.dk = (char *)a->dK;
     p.dv = (char *)a->dV;
     p.delta = (float *)workspace;
+    p.lse2 = (float *)((char *)workspace + need / 2);
     p.n_bh = (int)bh;
     p.n_q = (int)a->N_q;
     p.n_kv = (int)a->N_kv;

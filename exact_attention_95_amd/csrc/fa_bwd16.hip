@@ -231,7 +231,9 @@ __device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic (float32), D/8 lanes per row, 8 elements each.
+// D_i = sum_c dO_ic O_ic (float32), D/8 lanes per row, 8 elements each; the
+// same pass stores LSE_i log2(e), the exponent offset both gradient kernels
+// need per row.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
     typedef T T8 __attribute__((ext_vector_type(8)));
@@ -248,7 +250,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
-    if (row < n_rows && threadIdx.x % TPR == 0) p.delta[row] = acc;
+    if (row < n_rows && threadIdx.x % TPR == 0) {
+        p.delta[row] = acc;
+        p.lse2[row] = p.lse[row] * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     load_rows<C>(qh, qi, n_q, qf, h);
     load_rows<C>(gh, qi, n_q, gf, h);
     const int64_t row = (int64_t)bh * n_q + (qi < n_q ? qi : n_q - 1);
-    const float lse2 = p.lse[row] * kLog2e;
+    const float lse2 = p.lse2[row];
     const float dlt = p.delta[row];
     const float c = p.c;
     DropQuad dr{};
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
 
     const char *qh = p.q + (int64_t)bh * n_q * C::RB;
     const char *gh = p.dout + (int64_t)bh * n_q * C::RB;
-    const float *lh = p.lse + (int64_t)bh * n_q;
+    const float *lh = p.lse2 + (int64_t)bh * n_q;
     const float *dh = p.delta + (int64_t)bh * n_q;
 
     // query tiles [t0, ntile): causal rows before the block's first key see none of it
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int r = 8 * k2 + e;
-                const float l2 = (e < 4 ? l_lo[e & 3] : l_hi[e & 3]) * kLog2e;
+                const float l2 = e < 4 ? l_lo[e & 3] : l_hi[e & 3];
                 const float dl = e < 4 ? d_lo[e & 3] : d_hi[e & 3];
                 float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l2));
                 if (MK) {

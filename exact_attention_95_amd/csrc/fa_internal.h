@@ -67,6 +67,7 @@ struct BwdParams {
     char *dk;
     char *dv;
     float *delta;      // workspace: D_i = sum_c dO_ic O_ic, [n_bh * n_q]
+    float *lse2;       // workspace: LSE_i log2(e), [n_bh * n_q]
     int n_bh;
     int n_q;
     int n_kv;

@@ -216,8 +216,9 @@ typedef struct {
 int fa_bwd_validate(const fa_bwd_args *args);
 
 /*
- * Workspace bytes fa_bwd needs (float32 D, one value per query row, rounded
- * up to 256 bytes); -1 for arguments fa_bwd_validate rejects.  Host-only.
+ * Workspace bytes fa_bwd needs (float32 D and LSE log2(e), one value each
+ * per query row, each array rounded up to 256 bytes); -1 for arguments
+ * fa_bwd_validate rejects.  Host-only.
  */
 int64_t fa_bwd_workspace_bytes(const fa_bwd_args *args);
 
@@ -226,8 +227,9 @@ int64_t fa_bwd_workspace_bytes(const fa_bwd_args *args);
  * the caller, 256-byte aligned, at least fa_bwd_workspace_bytes(args) bytes,
  * not overlapping any argument buffer (FA_ERR_WORKSPACE / FA_ERR_ALIAS
  * otherwise); its contents are overwritten.  Three kernels run on
- * args->stream, in order: D from dO and O, then dQ (one workgroup per query
- * block), then dK and dV (one workgroup per key block).  No atomics: every
+ * args->stream, in order: D from dO and O (and LSE log2(e) from LSE), then dQ
+ * (one workgroup per query block), then dK and dV (one workgroup per key
+ * block).  No atomics: every
  * output element is written by exactly one lane, so results are bitwise
  * repeatable.
  */

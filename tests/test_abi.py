@@ -270,7 +270,7 @@ def test_bwd_validate_null_args_and_empty_problems():
 
 def test_bwd_workspace_bytes():
     a = good_bwd_args()
-    assert fa.fa_bwd_workspace_bytes(a) == -(-2 * 3 * 100 * 4 // 256) * 256
+    assert fa.fa_bwd_workspace_bytes(a) == 2 * (-(-2 * 3 * 100 * 4 // 256) * 256)  # D, LSE log2(e)
     assert fa.fa_bwd_workspace_bytes(good_bwd_args(d=256)) == -1
 
 
