@@ -265,6 +265,100 @@ def device_probe(dtype: str, stream) -> dict:
     }
 
 
+def sample_sclk_mhz():
+    """Current shader clock in MHz as rocm-smi reports it, or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                             timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for line in out.splitlines():
+        if "sclk" in line:
+            m = re.search(r"\((\d+)\s*Mhz\)", line, re.IGNORECASE)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+def timed_with_clock(fn, stream, seconds: float) -> dict:
+    """Runs fn back to back on `stream` for about `seconds` while a thread samples
+    the shader clock; returns ms per call (HIP events) and the median clock."""
+    import threading
+
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n = max(10, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+    clocks, done = [], threading.Event()
+
+    def sampler():
+        time.sleep(0.3)  # past the ramp at the start of the run
+        while not done.is_set():
+            c = sample_sclk_mhz()
+            if c is None:
+                return
+            clocks.append(c)
+            time.sleep(0.1)
+
+    th = threading.Thread(target=sampler)
+    e0.record(stream)
+    th.start()
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    done.set()
+    th.join()
+    return {"ms": round(e0.elapsed_time(e1) / n, 4), "calls": n,
+            "sclk_mhz_median": float(np.median(clocks)) if clocks else None,
+            "sclk_samples": len(clocks)}
+
+
+def power_check(w, step, q, k, v, stream, seconds: float = 2.0) -> dict:
+    """The same launches on the workload's seeded inputs and on all-zero inputs
+    (identical instruction stream, no data toggling), and hipBLASLt's
+    8192^3 bf16 GEMM (torch.matmul) on N(0,1) and on all-zero operands, each
+    run for about `seconds` with the shader clock sampled.  Tells a kernel
+    limited by its instruction stream from one limited by the power draw of
+    its data."""
+    import torch
+    rec = {"workload": w.name}
+    with torch.cuda.stream(stream):
+        rec["attention_seeded"] = timed_with_clock(step, stream, seconds)
+        saved = [t.clone() for t in (q, k, v)]
+        for t in (q, k, v):
+            t.zero_()
+        rec["attention_zeros"] = timed_with_clock(step, stream, seconds)
+        for t, s in zip((q, k, v), saved):
+            t.copy_(s)
+        del saved
+        for r in (rec["attention_seeded"], rec["attention_zeros"]):
+            r["tflops"] = round(w.flops / (r["ms"] * 1e-3) / 1e12, 1)
+        m = 8192
+        gen = torch.Generator(device=q.device).manual_seed(0)
+        a = torch.randn(m, m, device=q.device, generator=gen).to(torch.bfloat16)
+        b = torch.randn(m, m, device=q.device, generator=gen).to(torch.bfloat16)
+        c = torch.empty(m, m, device=q.device, dtype=torch.bfloat16)
+        rec["gemm8192_bf16_randn"] = timed_with_clock(lambda: torch.matmul(a, b, out=c), stream, seconds)
+        a.zero_()
+        b.zero_()
+        rec["gemm8192_bf16_zeros"] = timed_with_clock(lambda: torch.matmul(a, b, out=c), stream, seconds)
+        for key in ("gemm8192_bf16_randn", "gemm8192_bf16_zeros"):
+            rec[key]["tflops"] = round(2 * m ** 3 / (rec[key]["ms"] * 1e-3) / 1e12, 1)
+    torch.cuda.synchronize()
+    rec["attention_over_gemm_seeded"] = round(
+        rec["attention_seeded"]["tflops"] / rec["gemm8192_bf16_randn"]["tflops"], 4)
+    return rec
+
+
 def memory_report(names) -> list:
     """Device memory of fa_fwd (inputs, outputs and nothing else) against the
     analytic footprint of materialising S and P (N x N each, input dtype)."""
@@ -317,6 +411,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-launch (warm and cold-cache) timings and the device "
                          "probes that follow the timed region (for profiler runs)")
+    ap.add_argument("--power-check", action="store_true",
+                    help="time the forward on the seeded inputs and on all-zero inputs, and "
+                         "hipBLASLt's 8192^3 bf16 GEMM on N(0,1) and on zero operands, with the "
+                         "shader clock sampled, print one JSON line and exit")
     ap.add_argument("--memory-report", action="store_true",
                     help="print device memory of the long causal fp16 workloads vs a "
                          "materialised N x N baseline and exit")
@@ -400,6 +498,13 @@ def main(argv=None) -> int:
             s = fa.fa_bwd(bargs, bws.data_ptr(), bws.numel())
             if s != fa.FA_OK:
                 raise fa.FaError(s)
+
+    if args.power_check:
+        if args.bwd or splitkv is not None:
+            print("--power-check covers the single-pass forward", file=sys.stderr)
+            return 2
+        print(json.dumps(power_check(w, step, q, k, v, stream)), flush=True)
+        return 0
 
     torch.cuda.synchronize()
     for _ in range(args.warmup):
