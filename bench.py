@@ -411,6 +411,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-launch (warm and cold-cache) timings and the device "
                          "probes that follow the timed region (for profiler runs)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="time every compiled variant (tile shape) for the workload's dtype, "
+                         "head dim and mask, one JSON line each, and exit")
     ap.add_argument("--power-check", action="store_true",
                     help="time the forward on the seeded inputs and on all-zero inputs, and "
                          "hipBLASLt's 8192^3 bf16 GEMM on N(0,1) and on zero operands, with the "
@@ -498,6 +501,24 @@ def main(argv=None) -> int:
             s = fa.fa_bwd(bargs, bws.data_ptr(), bws.numel())
             if s != fa.FA_OK:
                 raise fa.FaError(s)
+
+    if args.tile_sweep:
+        if args.bwd or splitkv is not None:
+            print("--tile-sweep covers the single-pass forward", file=sys.stderr)
+            return 2
+        # each variant runs back to back for about a second, long enough for
+        # the board's power management to settle (short bursts run at a
+        # higher clock); two passes, so drift of the board shows
+        n_var = fa.fa_num_variants(fargs.dtype, w.d, w.causal)
+        for rep in range(2):
+            for tile in range(1, n_var + 1):
+                fargs.tile_override = tile
+                r = timed_with_clock(step, stream, 1.0)
+                print(json.dumps({"workload": w.name, "pass": rep, "tile_override": tile,
+                                  "variant": fa.fa_variant_name(fargs.dtype, w.d, w.causal, tile),
+                                  "default": tile == 1, **r,
+                                  "tflops": round(w.flops / (r["ms"] * 1e-3) / 1e12, 1)}), flush=True)
+        return 0
 
     if args.power_check:
         if args.bwd or splitkv is not None:
