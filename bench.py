@@ -48,6 +48,33 @@ def algorithmic_bytes(w) -> float:
     oe = 2 if w.dtype == "fp8_e4m3" else e
     per_head = (w.n_q * w.d * e + 2 * w.n_kv * w.d * e + w.n_q * w.d * oe + w.n_q * 4)
     return float(w.B * w.H * per_head)
+def materialised_bytes(w) -> float:
+    """HBM bytes of the standard three-step method ("FlashAttention 与显存",
+    plates 04 and 14): Q, K, V read and O written once, and the N_q x N_kv
+    matrices S and P each written once and read once, all in the input's
+    element size."""
+    e = ELEM_BYTES[w.dtype]
+    return float(w.B * w.H * e * ((2 * w.n_q + 2 * w.n_kv) * w.d + 4 * w.n_q * w.n_kv))
+
+
+def fa_bytes_without_l2(w, br: int) -> float:
+    """HBM bytes of the tiled method with no cache reuse ("FlashAttention 与显存",
+    plate 14, second-version order): each block of br query rows is read once
+    and reads all of K and V once; O is written once."""
+    e = ELEM_BYTES[w.dtype]
+    passes = -(-w.n_q // br)
+    return float(w.B * w.H * e * (2 * w.n_q * w.d + passes * 2 * w.n_kv * w.d))
+
+
+def variant_rows(name: str) -> int:
+    """Query rows per workgroup of a variant named br<waves>x<rows per wave>_..."""
+    import re
+    m = re.search(r"br(\d+)x(\d+)", name)
+    if not m:
+        raise ValueError("variant name without a row block: %r" % name)
+    return int(m.group(1)) * int(m.group(2))
+
+
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -596,6 +623,12 @@ def main(argv=None) -> int:
                                if splitkv is not None else
                                fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1)),
                    "flops_per_step": flops, "algorithmic_bytes_per_step": nbytes},
+        # HBM bytes the two traffic models of the pages give for this launch,
+        # beside the measured traffic (fwd only)
+        "traffic_models": None if args.bwd or splitkv is not None else {
+            "materialised_s_and_p": materialised_bytes(w),
+            "tiled_without_cache_reuse": fa_bytes_without_l2(w, variant_rows(
+                fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1)))},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": stored_traffic(w.name, w.dtype, args.bwd),
