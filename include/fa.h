@@ -13,6 +13,17 @@
  * computed tile by tile with the online softmax, so S and P never reach HBM.
  * The result equals the definition up to floating-point rounding.
  *
+ * Very long key ranges.  The single-pass forward adds each key tile's share
+ * to float32 running sums per row (the row sum and the output accumulator),
+ * once per tile.  When much of a row's softmax mass is spread thinly over a
+ * very long key range, each addition rounds away a part of a small addend,
+ * and the error grows with the number of tiles: with 2^24 keys of which the
+ * low-score majority carries 2-12 % of the mass, O is off by about 1e-2 and
+ * LSE by about 6e-3.  fa_fwd_splitkv sums short chunks and merges them, and
+ * stays at ordinary rounding there (O relative L2 2e-3, LSE 2e-5 measured);
+ * use it for key ranges of millions of keys.  Byte offsets are 64-bit
+ * throughout: tensors larger than 4 GiB are supported.
+ *
  * Layout.  Q is [B, H, N_q, d]; K and V are [B, H, N_kv, d]; O is
  * [B, H, N_q, d]; LSE is [B, H, N_q].  All are dense row-major with d the
  * fastest dimension (the per-(batch, head) [N, d] slices of the section-2

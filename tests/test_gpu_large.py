@@ -1,0 +1,169 @@
+"""Tensors past 4 GiB, at the library's largest sizes.
+
+Every global offset in the kernels is formed in 64-bit arithmetic: per head
+(b*H + h)*N*row_bytes, and within a head tile_start*row_bytes.  These tests
+put the data that decides the result beyond the 2 GiB and 4 GiB byte offsets,
+where a 32-bit offset would wrap.
+
+- Keys past 4 GiB: one head with 2^24 + 37 keys (K and V 4 GiB each).  All
+  keys are zero rows with V = 1/4, except five "special" keys at byte offsets
+  768, 2 GiB + 1280, 4 GiB - 256, 4 GiB and the last row, whose large scores
+  carry the softmax mass (each dominates some rows).  O and LSE then have an
+  exact closed form (plain softmax attention evaluated in fp64 over the five
+  specials plus n_zero equal keys).  With scores of about 39 the zero keys'
+  share is below 1e-8 and both entry points must match; with scores of about
+  18 the zero keys carry 2-12 % spread over 2^24 keys, which the single-pass
+  kernel's float32 running sums cannot hold to the bar (see the test), and
+  the split-KV entry point must match.
+- Queries past 4 GiB: two heads of 2^24 + 2^22 + 3 queries (Q and O 5 GiB
+  each), with sampled rows around the 2 GiB and 4 GiB offsets checked against
+  the fp64 oracle, with and without the causal mask.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import gpu_available
+from exact_attention_95_amd import fa
+import oracle
+from parity import LSE_TOL, TOL, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+GIB = 1 << 30
+
+
+def require_device_bytes(n: int):
+    free, _ = torch.cuda.mem_get_info()
+    if free < n + 2 * GIB:
+        pytest.skip("needs %.1f GiB of free device memory" % (n / GIB))
+
+
+def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, label: str):
+    o = o_gpu.float().cpu().double().numpy().reshape(o_ref.shape)
+    lse = lse_gpu.float().cpu().double().numpy().reshape(lse_ref.shape)
+    diff = o - o_ref
+    err = {"max_abs": float(np.abs(diff).max()),
+           "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(o_ref)),
+           "lse_max_abs": float(np.abs(lse - lse_ref).max())}
+    say(label, err)
+    max_abs, rel = TOL[dtype]
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), label
+    assert err["max_abs"] <= max_abs and err["rel_l2"] <= rel, (label, err)
+    assert err["lse_max_abs"] <= LSE_TOL, (label, err)
+
+
+def keys_past_4gib_case(big: float):
+    """One head of 2^24 + 37 keys: zero rows with V = 1/4, and five special
+    keys whose first component is `big` (Q's first component is 1), at byte
+    offsets 768, 2 GiB + 1280, 4 GiB - 256, 4 GiB and the last row.  Returns
+    the device tensors, the scale, and O, LSE and the zero keys' share of the
+    softmax mass in closed form (fp64)."""
+    n_q, n_kv, d = 33, (1 << 24) + 37, 128
+    require_device_bytes(2 * n_kv * d * 2)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    g = torch.Generator().manual_seed(95)
+    q = torch.randn(n_q, d, generator=g)
+    q[:, 0] = 1.0
+    q = q.to(torch.bfloat16)
+    special = [3, (1 << 23) + 5, (1 << 24) - 1, 1 << 24, n_kv - 1]
+    ks = torch.randn(len(special), d, generator=g)
+    ks[:, 0] = big  # the random part of the score decides which special dominates a row
+    ks = ks.to(torch.bfloat16)
+    vs = torch.randn(len(special), d, generator=g).to(torch.bfloat16)
+    v_zero = 0.25
+    say("keys past 4 GiB: n_kv", n_kv, "special rows", special, "big", big)
+    k = torch.zeros(1, 1, n_kv, d, dtype=torch.bfloat16, device="cuda")
+    v = torch.full((1, 1, n_kv, d), v_zero, dtype=torch.bfloat16, device="cuda")
+    idx = torch.tensor(special, device="cuda")
+    k[0, 0, idx] = ks.cuda()
+    v[0, 0, idx] = vs.cuda()
+
+    # closed form in fp64: the specials' scores, and n_zero keys of score 0, value v_zero
+    q64, k64, v64 = q.double().numpy(), ks.double().numpy(), vs.double().numpy()
+    s = scale * (q64 @ k64.T)                                   # [n_q, 5]
+    n_zero = n_kv - len(special)
+    m = np.maximum(s.max(axis=1), 0.0)
+    w = np.exp(s - m[:, None])
+    w0 = n_zero * np.exp(-m)
+    ell = w0 + w.sum(axis=1)
+    o_ref = (w0[:, None] * v_zero + w @ v64) / ell[:, None]
+    lse_ref = m + np.log(ell)
+    # each special matters: reading any one of them wrong (here: as a zero row)
+    # moves O by far more than the tolerance
+    for j in range(len(special)):
+        w_drop = w.copy()
+        w_drop[:, j] = 0.0
+        w0_drop = w0 + np.exp(-m)
+        o_drop = (w0_drop[:, None] * v_zero + w_drop @ v64) / (w0_drop + w_drop.sum(axis=1))[:, None]
+        assert np.abs(o_drop - o_ref).max() > 0.5
+    return q.cuda()[None, None], k, v, scale, o_ref, lse_ref, w0 / ell
+
+
+def test_keys_past_4gib_closed_form():
+    # scores about 39: the 2^24 zero-score keys carry under 1e-8 of the mass,
+    # so the result depends on the five specials being read from the right
+    # addresses, not on how the long tail is summed
+    q, k, v, scale, o_ref, lse_ref, tail = keys_past_4gib_case(440.0)
+    assert tail.max() < 1e-8
+    o, lse = fa.fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "single pass")
+    o, lse = fa.fwd_splitkv(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "split-KV")
+
+
+def test_long_tail_over_2_24_keys_split_kv():
+    # scores about 18: the zero-score keys carry 2-12 % of the mass, spread
+    # over 2^24 keys.  The single-pass kernel adds each 64-key tile's share to
+    # one float32 running sum per row, 2^18 times, and each addition rounds
+    # away a fixed part of a small addend (here about 2 ulps of the sum), so
+    # its error grows with the number of key tiles; split-KV sums short
+    # chunks and merges them, and meets the bar.
+    q, k, v, scale, o_ref, lse_ref, tail = keys_past_4gib_case(200.0)
+    assert tail.max() > 1e-2 and tail.min() < 0.5
+    o, lse = fa.fwd_splitkv(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "split-KV, long tail")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_queries_past_4gib_sampled_rows(causal):
+    B, H, n_q, n_kv, d = 1, 2, (1 << 24) + (1 << 22) + 3, 100, 64
+    require_device_bytes(2 * B * H * n_q * d * 2)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    gd = torch.Generator(device="cuda").manual_seed(7 + int(causal))
+    q = torch.randn(B, H, n_q, d, generator=gd, device="cuda", dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(11)
+    k = torch.randn(B, H, n_kv, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, n_kv, d, generator=g).to(torch.bfloat16)
+    say("queries past 4 GiB: n_q", n_q, "causal", causal)
+    o, lse = fa.fwd(q, k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(3)
+    fixed = [0, 1, n_kv - 2, n_kv - 1, n_kv, 1 << 23, (1 << 24) - 1, 1 << 24, n_q - 2, n_q - 1]
+    for h in range(H):
+        local = np.unique(np.concatenate([fixed, rng.integers(0, n_q, 20)]))
+        o_rows = o[0, h, torch.from_numpy(local).cuda()]
+        lse_rows = lse[0, h, torch.from_numpy(local).cuda()]
+        # rows at or past n_kv - 1 see every key under either mask; earlier
+        # causal rows are checked against the oracle on the head's first n_kv queries
+        late = local >= n_kv - 1 if causal else np.ones(local.size, bool)
+        o_ref = np.empty((local.size, d))
+        lse_ref = np.empty(local.size)
+        if late.any():
+            qr = q[0, h, torch.from_numpy(local[late]).cuda()].cpu()
+            o_ref[late], lse_ref[late] = oracle.attention(qr, k[0, h], v[0, h], scale, causal=False)
+        if (~late).any():
+            qh = q[0, h, :n_kv].cpu()
+            o_ref[~late], lse_ref[~late] = oracle.attention(
+                qh[None, None], k[0, h][None, None], v[0, h][None, None], scale, causal=True,
+                rows=local[~late])
+        say("head", h, "rows", local.size, "max byte offset of a checked row: %.2f GiB"
+            % ((h * n_q + local.max()) * d * 2 / GIB))
+        check(o_rows, lse_rows, o_ref, lse_ref, "bf16", "head %d causal %s" % (h, causal))
