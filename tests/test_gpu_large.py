@@ -37,6 +37,7 @@ GIB = 1 << 30
 
 
 def require_device_bytes(n: int):
+    torch.cuda.empty_cache()  # blocks cached by earlier tests count as used
     free, _ = torch.cuda.mem_get_info()
     if free < n + 2 * GIB:
         pytest.skip("needs %.1f GiB of free device memory" % (n / GIB))
