@@ -292,26 +292,48 @@ def device_probe(dtype: str, stream) -> dict:
     }
 
 
-def sample_sclk_mhz():
-    """Current shader clock in MHz as rocm-smi reports it, or None."""
+def hwmon_power_files():
+    """(power1_input, power1_cap) sysfs paths of the first GPU that has them
+    (values in microwatts), or (None, None)."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")):
+        cap = f.replace("power1_input", "power1_cap")
+        return f, (cap if os.path.exists(cap) else None)
+    return None, None
+
+
+def read_watts(path):
+    try:
+        with open(path) as f:
+            return int(f.read().strip()) / 1e6
+    except (OSError, ValueError, TypeError):
+        return None
+
+
+def sample_sclk_power():
+    """(shader clock in MHz as rocm-smi reports it, package power in W from
+    the GPU's hwmon sysfs file); None for a value that is not available."""
     import re
     import subprocess
+    clk = None
     try:
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
                              timeout=10).stdout
+        for line in out.splitlines():
+            if "sclk" in line:
+                m = re.search(r"\((\d+)\s*Mhz\)", line, re.IGNORECASE)
+                if m:
+                    clk = int(m.group(1))
+                    break
     except (OSError, subprocess.SubprocessError):
-        return None
-    for line in out.splitlines():
-        if "sclk" in line:
-            m = re.search(r"\((\d+)\s*Mhz\)", line, re.IGNORECASE)
-            if m:
-                return int(m.group(1))
-    return None
+        pass
+    return clk, read_watts(hwmon_power_files()[0])
 
 
 def timed_with_clock(fn, stream, seconds: float) -> dict:
     """Runs fn back to back on `stream` for about `seconds` while a thread samples
-    the shader clock; returns ms per call (HIP events) and the median clock."""
+    the shader clock and package power; returns ms per call (HIP events) and
+    their medians."""
     import threading
 
     import torch
@@ -324,15 +346,18 @@ def timed_with_clock(fn, stream, seconds: float) -> dict:
     e1.record(stream)
     torch.cuda.synchronize()
     n = max(10, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
-    clocks, done = [], threading.Event()
+    clocks, watts, done = [], [], threading.Event()
 
     def sampler():
         time.sleep(0.3)  # past the ramp at the start of the run
         while not done.is_set():
-            c = sample_sclk_mhz()
-            if c is None:
+            c, w = sample_sclk_power()
+            if c is None and w is None:
                 return
-            clocks.append(c)
+            if c is not None:
+                clocks.append(c)
+            if w is not None:
+                watts.append(w)
             time.sleep(0.1)
 
     th = threading.Thread(target=sampler)
@@ -346,7 +371,8 @@ def timed_with_clock(fn, stream, seconds: float) -> dict:
     th.join()
     return {"ms": round(e0.elapsed_time(e1) / n, 4), "calls": n,
             "sclk_mhz_median": float(np.median(clocks)) if clocks else None,
-            "sclk_samples": len(clocks)}
+            "sclk_samples": len(clocks),
+            "power_w_median": float(np.median(watts)) if watts else None}
 
 
 def power_check(w, step, q, k, v, stream, seconds: float = 2.0) -> dict:
@@ -357,7 +383,7 @@ def power_check(w, step, q, k, v, stream, seconds: float = 2.0) -> dict:
     limited by its instruction stream from one limited by the power draw of
     its data."""
     import torch
-    rec = {"workload": w.name}
+    rec = {"workload": w.name, "power_cap_w": read_watts(hwmon_power_files()[1])}
     with torch.cuda.stream(stream):
         rec["attention_seeded"] = timed_with_clock(step, stream, seconds)
         saved = [t.clone() for t in (q, k, v)]
