@@ -19,6 +19,8 @@ where a 32-bit offset would wrap.
   each), with sampled rows around the 2 GiB and 4 GiB offsets checked against
   the fp64 oracle, with and without the causal mask; and the same with E4M3
   inputs at d = 128 (Q 5 GiB, O in bf16 10 GiB).
+- Backward past 4 GiB: the same two heads (Q, O, dO and dQ 5 GiB each);
+  dQ of sampled rows against the oracle's gradients, dK and dV finite.
 """
 import math
 
@@ -29,7 +31,7 @@ import torch
 from conftest import gpu_available
 from exact_attention_95_amd import fa
 import oracle
-from parity import LSE_TOL, TOL, say
+from parity import BWD_TOL, LSE_TOL, TOL, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -199,3 +201,37 @@ def test_e4m3_queries_past_4gib_sampled_rows():
         say("head", h, "rows", local.size, "max byte offset of a checked O row: %.2f GiB"
             % ((h * n_q + local.max()) * d * 2 / GIB))
         check(o[0, h, sel], lse[0, h, sel], o_ref, lse_ref, "fp8_e4m3", "E4M3 head %d" % h)
+
+
+def test_backward_queries_past_4gib_sampled_rows():
+    B, H, n_q, n_kv, d = 1, 2, (1 << 24) + (1 << 22) + 3, 100, 64
+    require_device_bytes(4 * B * H * n_q * d * 2)  # Q, O, dO, dQ
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    gd = torch.Generator(device="cuda").manual_seed(31)
+    q = torch.randn(B, H, n_q, d, generator=gd, device="cuda", dtype=torch.bfloat16)
+    do = torch.randn(B, H, n_q, d, generator=gd, device="cuda", dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(17)
+    k = torch.randn(B, H, n_kv, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, n_kv, d, generator=g).to(torch.bfloat16)
+    kd, vd = k.cuda(), v.cuda()
+    say("backward past 4 GiB: n_q", n_q)
+    o, lse = fa.fwd(q, kd, vd, scale=scale)
+    dq, dk, dv = fa.bwd(q, kd, vd, o, lse, do, scale=scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(dk.float()).all()) and bool(torch.isfinite(dv.float()).all())
+    rng = np.random.default_rng(9)
+    fixed = [0, 1, 1 << 23, (1 << 24) - 1, 1 << 24, n_q - 2, n_q - 1]
+    for h in range(H):
+        local = np.unique(np.concatenate([fixed, rng.integers(0, n_q, 20)]))
+        sel = torch.from_numpy(local).cuda()
+        # rows are independent without the mask: the selected rows form a problem of their own
+        q_rows, do_rows = q[0, h, sel].cpu(), do[0, h, sel].cpu()
+        dq_ref, _, _ = oracle.backward(q_rows, k[0, h], v[0, h], do_rows, scale,
+                                       rows=np.arange(local.size), keys=np.zeros(0, np.int64))
+        got = dq[0, h, sel].float().cpu().double().numpy()
+        err_max = float(np.abs(got - dq_ref).max() / np.abs(dq_ref).max())
+        err_l2 = float(np.linalg.norm(got - dq_ref) / np.linalg.norm(dq_ref))
+        say("head", h, "rows", local.size, "dQ max err / max |ref| %.2e, rel L2 %.2e, last row at %.2f GiB"
+            % (err_max, err_l2, (h * n_q + local.max()) * d * 2 / GIB))
+        assert np.isfinite(got).all()
+        assert err_max <= BWD_TOL[0] and err_l2 <= BWD_TOL[1], (h, err_max, err_l2)
