@@ -375,31 +375,39 @@ def timed_with_clock(fn, stream, seconds: float) -> dict:
             "power_w_median": float(np.median(watts)) if watts else None}
 
 
-def power_check(w, step, q, k, v, stream, seconds: float = 2.0) -> dict:
+def power_check(w, step, inputs, stream, flops: float, refresh=None, pass_name: str = "fwd",
+                seconds: float = 2.0) -> dict:
     """The same launches on the workload's seeded inputs and on all-zero inputs
     (identical instruction stream, no data toggling), and hipBLASLt's
     8192^3 bf16 GEMM (torch.matmul) on N(0,1) and on all-zero operands, each
-    run for about `seconds` with the shader clock sampled.  Tells a kernel
-    limited by its instruction stream from one limited by the power draw of
-    its data."""
+    run for about `seconds` with the shader clock and package power sampled.
+    Tells a kernel limited by its instruction stream from one limited by the
+    power draw of its data.  `inputs` are the tensors zeroed; `refresh`, if
+    given, recomputes what the step reads besides them (the backward reads the
+    forward's O and LSE) after they change."""
     import torch
-    rec = {"workload": w.name, "power_cap_w": read_watts(hwmon_power_files()[1])}
+    rec = {"workload": w.name, "pass": pass_name, "power_cap_w": read_watts(hwmon_power_files()[1])}
     with torch.cuda.stream(stream):
         rec["attention_seeded"] = timed_with_clock(step, stream, seconds)
-        saved = [t.clone() for t in (q, k, v)]
-        for t in (q, k, v):
+        saved = [t.clone() for t in inputs]
+        for t in inputs:
             t.zero_()
+        if refresh:
+            refresh()
         rec["attention_zeros"] = timed_with_clock(step, stream, seconds)
-        for t, s in zip((q, k, v), saved):
+        for t, s in zip(inputs, saved):
             t.copy_(s)
+        if refresh:
+            refresh()
         del saved
         for r in (rec["attention_seeded"], rec["attention_zeros"]):
-            r["tflops"] = round(w.flops / (r["ms"] * 1e-3) / 1e12, 1)
+            r["tflops"] = round(flops / (r["ms"] * 1e-3) / 1e12, 1)
         m = 8192
-        gen = torch.Generator(device=q.device).manual_seed(0)
-        a = torch.randn(m, m, device=q.device, generator=gen).to(torch.bfloat16)
-        b = torch.randn(m, m, device=q.device, generator=gen).to(torch.bfloat16)
-        c = torch.empty(m, m, device=q.device, dtype=torch.bfloat16)
+        dev = inputs[0].device
+        gen = torch.Generator(device=dev).manual_seed(0)
+        a = torch.randn(m, m, device=dev, generator=gen).to(torch.bfloat16)
+        b = torch.randn(m, m, device=dev, generator=gen).to(torch.bfloat16)
+        c = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
         rec["gemm8192_bf16_randn"] = timed_with_clock(lambda: torch.matmul(a, b, out=c), stream, seconds)
         a.zero_()
         b.zero_()
@@ -539,6 +547,7 @@ def main(argv=None) -> int:
             print("the backward covers bf16/fp16 with d in {64, 128}", file=sys.stderr)
             return 2
         # the forward's O and LSE, then the timed step is one fa_bwd call
+        fwd_step = step
         step()
         do = make_dout(w).to(dev)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -574,10 +583,15 @@ def main(argv=None) -> int:
         return 0
 
     if args.power_check:
-        if args.bwd or splitkv is not None:
-            print("--power-check covers the single-pass forward", file=sys.stderr)
+        if splitkv is not None:
+            print("--power-check covers the single-pass forward and the backward", file=sys.stderr)
             return 2
-        print(json.dumps(power_check(w, step, q, k, v, stream)), flush=True)
+        if args.bwd:
+            rec = power_check(w, step, (q, k, v, do), stream, w.bwd_flops, refresh=fwd_step,
+                              pass_name="bwd")
+        else:
+            rec = power_check(w, step, (q, k, v), stream, w.flops)
+        print(json.dumps(rec), flush=True)
         return 0
 
     torch.cuda.synchronize()
