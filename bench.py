@@ -622,6 +622,13 @@ def main(argv=None) -> int:
         extras["launch_ms"]["cold"]["flush_bytes"] = flush.numel()
         del flush
         extras["device"] = device_probe(w.dtype, stream)
+        # shader clock and package power while the same step runs back to back
+        # for about a second (random data: the board's power cap sets the clock)
+        under = timed_with_clock(step, stream, 1.0)
+        extras["device"]["under_kernel"] = {
+            "ms": under["ms"], "sclk_mhz_median": under["sclk_mhz_median"],
+            "power_w_median": under["power_w_median"],
+            "power_cap_w": read_watts(hwmon_power_files()[1])}
 
     if args.copy_calibration:
         # a plain device-to-device copy of exactly 1 GiB (hipMemcpy's copy kernel)
