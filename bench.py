@@ -420,6 +420,33 @@ def power_check(w, step, inputs, stream, flops: float, refresh=None, pass_name: 
     return rec
 
 
+def hbm_reference(dev, nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """GB/s of torch's device copy (bytes read + written) and of a float32 sum
+    over bf16 data (bytes read), each on `nbytes` of input."""
+    import torch
+    x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    y = torch.empty_like(x)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+
+    def rate(fn, moved):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    rec = {"bytes": nbytes,
+           "copy_GBps": rate(lambda: y.copy_(x), 2 * nbytes),
+           "sum_read_GBps": rate(lambda: acc.copy_(x.sum(dtype=torch.float32)), nbytes)}
+    del x, y
+    return rec
+
+
 def memory_report(names) -> list:
     """Device memory of fa_fwd (inputs, outputs and nothing else) against the
     analytic footprint of materialising S and P (N x N each, input dtype)."""
@@ -681,6 +708,10 @@ def main(argv=None) -> int:
                      "traffic": stored_traffic(w.name, w.dtype, args.bwd),
                      "kernel_ms": round(kernel_ms, 4)},
     }
+    if extras and hbm_bound:
+        # what torch's own streaming kernels reach on this HBM, for scale: a
+        # device copy (read + write) and a float32 sum (read), 4 GiB each
+        extras["hbm_reference"] = hbm_reference(dev)
     if extras:
         rec.update(extras)
         if not hbm_bound:
