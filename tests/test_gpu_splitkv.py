@@ -2,8 +2,7 @@
 
 The key range of every head is cut into chunks whose float32 partials are
 merged on the GPU; the result must match the plain definition (the oracle's
-three-pass attention) to the same tolerances as the single-pass kernel.
-"""
+three-pass attention) to the same tolerances as the single-pass kernel."""
 import numpy as np
 import pytest
 import torch
@@ -28,6 +27,11 @@ CASES = [
     (1, 2, 300, 300, 128, "bf16", True, 3),
     (1, 1, 200, 700, 64, "f16", True, 4),
     (1, 1, 700, 200, 64, "bf16", True, 2),
+    # one query row per head (decode shapes), ragged key counts, clamped chunk counts
+    (2, 3, 1, 3001, 64, "f16", False, 3),
+    (1, 2, 1, 70001, 128, "bf16", False, 0),
+    (1, 1, 1, 100, 64, "f16", False, 1000),
+    (3, 1, 1, 129, 128, "f16", False, 2),
 ]
 
 
@@ -91,3 +95,20 @@ def test_decode_workload_sampled_heads():
     err = errors(o_s, l_s, o_ref, lse_ref)
     say(err)
     assert_within(w, err, "decode sampled")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.5])
+def test_decode_scales(scale):
+    """One query row per head (decode): zero, negative and large scales
+    against the oracle and the single-pass kernel."""
+    w, x = random_problem(330, 2, 2, 1, 1000, 128, "bf16", False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = fa.fwd_splitkv(q, k, v, scale=scale, num_splits=5)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], scale, False)
+    err = errors(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref)
+    say(scale, err)
+    assert_within(w, err, "scale %g" % scale)
+    o1, l1 = fa.fwd(q, k, v, scale=scale)
+    assert (o1.float() - o.float()).abs().max().item() <= 2e-2
+    assert (l1 - lse).abs().max().item() <= 1e-3
