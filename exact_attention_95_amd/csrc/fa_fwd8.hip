@@ -18,6 +18,11 @@
 //   O = O_acc dv / l   stored as bfloat16 (the 2^6 cancels);
 //   LSE = (m - 6 + log2 l) ln 2
 //
+// The softmax of each tile is split at its 32-key block boundary: block 0
+// runs under the PV MFMAs of the previous tile, block 1 under the S MFMAs of
+// the next, so the VALU work (here larger than the MFMA time of a wave) is
+// spread over both halves of the loop.
+//
 // Key order inside a 32-key block: row rho of the S^T MFMA is key
 // pi(rho) = 16 ((rho/4) % 2) + 4 (rho/8) + rho % 4, which makes the S^T
 // registers of each half-wave hold 16 consecutive keys, so the V^T operand
@@ -127,15 +132,20 @@ __device__ __forceinline__ void mask8(f32x16 (&s)[C::KB], int t0, int qi, int n_
         }
 }
 
-// Online-softmax step (plate 08 merge): the reference max is raised when the
-// tile's row max exceeds it by more than TAU (wave-uniform decision), so
-// P = exp2(S c - m) <= 2^TAU; the kernel computes P' = 2^PSHIFT P =
-// exp2(S c - m + PSHIFT) directly, sums the float32 P' into l_acc and rounds
-// P' to E4M3 into the P^T operand; `raised` and alpha tell the caller to
-// rescale O before accumulating this tile.
+// Online-softmax step (plate 08 merge) for one tile, in two parts at the
+// 32-key block boundary.  The reference max is raised when the tile's row max
+// exceeds it by more than TAU (wave-uniform decision), so P = exp2(S c - m) <=
+// 2^TAU; the kernel computes P' = 2^PSHIFT P = exp2(S c - m + PSHIFT)
+// directly, sums the float32 P' into l_acc and rounds P' to E4M3 into the P^T
+// operand; `raised` and alpha tell the caller to rescale O before
+// accumulating this tile.  softmax8_head takes the row max, the decision and
+// block 0 of P' (words 0-3 of the operand); softmax8_tail block 1 (words 4-7)
+// with the same bias.  The loop runs the head under the PV MFMAs of the
+// previous tile and the tail under the S MFMAs of the next, so both halves of
+// the loop carry VALU work (one max per tile, no extra instructions).
 template <class C>
-__device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m_use, float &l_acc,
-                                         float &alpha, bool &raised, float c) {
+__device__ __forceinline__ void softmax8_head(f32x16 (&s)[C::KB], i32x8 &pb, float &m_use, float &l_acc,
+                                              float &alpha, bool &raised, float c, float &bias) {
     float m4[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -149,22 +159,37 @@ __device__ __forceinline__ void softmax8(f32x16 (&s)[C::KB], i32x8 &pb, float &m
     alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_use - m_new);
     l_acc *= alpha;
     m_use = m_new;
-    const float bias = C::PSHIFT - ((m_use == kNegInf) ? 0.f : m_use);
+    bias = C::PSHIFT - ((m_use == kNegInf) ? 0.f : m_use);
     float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+    for (int w4 = 0; w4 < 4; ++w4) {
+        float v[4];
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * w4 + e], c, bias));
-                l4[e] += v[e];
-            }
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
-            pb[4 * kb + w4] = word;
+        for (int e = 0; e < 4; ++e) {
+            v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][4 * w4 + e], c, bias));
+            l4[e] += v[e];
         }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+        pb[w4] = word;
+    }
+    l_acc += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+}
+template <class C>
+__device__ __forceinline__ void softmax8_tail(const f32x16 &s1, i32x8 &pb, float &l_acc, float c, float bias) {
+    float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[4 * w4 + e], c, bias));
+            l4[e] += v[e];
+        }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+        pb[4 + w4] = word;
+    }
     l_acc += (l4[0] + l4[1]) + (l4[2] + l4[3]);
 }
 
@@ -255,11 +280,14 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
 
     wait_vm();
     __syncthreads();
+    f32x16 s_tail = (f32x16){};  // block 1 of the last tile's scores
+    float bias_tail = 0.f;        // and the exponent bias of its P'
     if (wn > 0) {
         f32x16 s[C::KB];
         qk8<C>(s, kbuf(0), koff, qf);
         if (need_mask(0)) mask8<C>(s, 0, qi, n_kv, h);
-        softmax8<C>(s, p0, m_use, l_acc, alpha, raised, c);
+        softmax8_head<C>(s, p0, m_use, l_acc, alpha, raised, c, bias_tail);
+        s_tail = s[1];
         raised = false;
     }
 
@@ -276,11 +304,18 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
         }
         if (t + 1 < wn) {
             f32x16 s[C::KB];
+            const bool masked = need_mask(t + 1);
             qk8<C>(s, kbuf(1 - PAR), koff, qf);
-            if (need_mask(t + 1)) mask8<C>(s, (t + 1) * C::BC, qi, n_kv, h);
+            softmax8_tail<C>(s_tail, pc, l_acc, c, bias_tail);
+            // keep the tail under the S MFMAs: without this the compiler
+            // sinks it past the masking branch, next to the PV MFMAs
+            asm volatile("" : "+v"(pc), "+v"(l_acc));
+            if (masked) mask8<C>(s, (t + 1) * C::BC, qi, n_kv, h);
             pv8<C>(o, vbuf(PAR), voff, pc);
-            softmax8<C>(s, pn, m_use, l_acc, alpha, raised, c);
+            softmax8_head<C>(s, pn, m_use, l_acc, alpha, raised, c, bias_tail);
+            s_tail = s[1];
         } else {
+            softmax8_tail<C>(s_tail, pc, l_acc, c, bias_tail);
             pv8<C>(o, vbuf(PAR), voff, pc);
         }
     };
