@@ -173,7 +173,8 @@ def test_queries_past_4gib_sampled_rows(causal):
         check(o_rows, lse_rows, o_ref, lse_ref, "bf16", "head %d causal %s" % (h, causal))
 
 
-def test_e4m3_queries_past_4gib_sampled_rows():
+@pytest.mark.parametrize("causal", [False, True])
+def test_e4m3_queries_past_4gib_sampled_rows(causal):
     B, H, n_q, n_kv, d = 1, 2, (1 << 24) + (1 << 22) + 3, 100, 128
     require_device_bytes(B * H * n_q * d * (2 + 1 + 2))  # bf16 draw, E4M3 codes, bf16 O
     scale = float(np.float32(1.0 / math.sqrt(d)))
@@ -186,21 +187,30 @@ def test_e4m3_queries_past_4gib_sampled_rows():
     g = torch.Generator().manual_seed(13)
     k = (torch.randn(B, H, n_kv, d, generator=g) * mul).clamp(-448, 448).to(torch.float8_e4m3fn)
     v = (torch.randn(B, H, n_kv, d, generator=g) * mul).clamp(-448, 448).to(torch.float8_e4m3fn)
-    say("E4M3 queries past 4 GiB: n_q", n_q)
-    o, lse = fa.fwd(q, k.cuda(), v.cuda(), scale=scale, descale=(descale, descale, descale))
+    say("E4M3 queries past 4 GiB: n_q", n_q, "causal", causal)
+    o, lse = fa.fwd(q, k.cuda(), v.cuda(), scale=scale, causal=causal, descale=(descale, descale, descale))
     torch.cuda.synchronize()
     assert o.dtype == torch.bfloat16
     rng = np.random.default_rng(5)
-    fixed = [0, 1, 1 << 23, (1 << 24) - 1, 1 << 24, n_q - 2, n_q - 1]
+    fixed = [0, 1, n_kv - 2, n_kv - 1, 1 << 23, (1 << 24) - 1, 1 << 24, n_q - 2, n_q - 1]
     for h in range(H):
         local = np.unique(np.concatenate([fixed, rng.integers(0, n_q, 20)]))
         sel = torch.from_numpy(local).cuda()
-        q_rows = oracle.dequant_e4m3(q[0, h, sel].cpu(), descale)
-        o_ref, lse_ref = oracle.attention(q_rows, oracle.dequant_e4m3(k[0, h], descale),
-                                          oracle.dequant_e4m3(v[0, h], descale), scale)
+        kh, vh = oracle.dequant_e4m3(k[0, h], descale), oracle.dequant_e4m3(v[0, h], descale)
+        # rows at or past n_kv - 1 see every key under either mask; earlier
+        # causal rows against the oracle on the head's first n_kv queries
+        late = local >= n_kv - 1 if causal else np.ones(local.size, bool)
+        o_ref, lse_ref = np.empty((local.size, d)), np.empty(local.size)
+        if late.any():
+            q_rows = oracle.dequant_e4m3(q[0, h, torch.from_numpy(local[late]).cuda()].cpu(), descale)
+            o_ref[late], lse_ref[late] = oracle.attention(q_rows, kh, vh, scale)
+        if (~late).any():
+            qh = oracle.dequant_e4m3(q[0, h, :n_kv].cpu(), descale)
+            o_ref[~late], lse_ref[~late] = oracle.attention(qh[None, None], kh[None, None], vh[None, None],
+                                                            scale, causal=True, rows=local[~late])
         say("head", h, "rows", local.size, "max byte offset of a checked O row: %.2f GiB"
             % ((h * n_q + local.max()) * d * 2 / GIB))
-        check(o[0, h, sel], lse[0, h, sel], o_ref, lse_ref, "fp8_e4m3", "E4M3 head %d" % h)
+        check(o[0, h, sel], lse[0, h, sel], o_ref, lse_ref, "fp8_e4m3", "E4M3 head %d causal %s" % (h, causal))
 
 
 def test_backward_queries_past_4gib_sampled_rows():
