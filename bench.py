@@ -110,13 +110,73 @@ def stored_traffic(workload: str, dtype: str, bwd: bool = False):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x, target_s: float = 15.0) -> dict:
-    """The fp64 oracle (as it stands) on a bounded row sample of the same workload.
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
-    Rows are drawn uniformly without replacement over all B*H*N_q rows; a
-    sample grows from 1024 rows until one run takes about target_s seconds of
-    host time (capped at the whole workload); the last run is reported.
-    """
+
+def oracle_operands(w, x):
+    """The exact values the kernel reads, as the oracle's inputs (E4M3: code x descale)."""
+    import oracle
+    if w.dtype == "fp8_e4m3":
+        dq, dk, dv = x["descale"]
+        return tuple(oracle.dequant_e4m3(t, s) for t, s in ((x["q"], dq), (x["k"], dk), (x["v"], dv)))
+    return x["q"], x["k"], x["v"]
+
+
+# parity bars of the forward: O max abs, O relative L2 over the compared
+# rows, LSE max abs (None: not part of the bar for the dtype)
+PARITY_BARS = {"f32": (1e-5, 1e-6, 1e-3), "f16": (2e-2, 5e-3, 1e-3), "bf16": (2e-2, 5e-3, 1e-3),
+               "fp8_e4m3": (None, 5e-2, 1e-3)}
+
+
+def one_thread_timings() -> dict:
+    """The oracle on one thread: the 1x1x256x64 float32 workload whole, and
+    one whole head (1024 rows) of the GPT-2-medium bf16 workload."""
+    import oracle
+    import torch
+    from exact_attention_95_amd.inputs import WORKLOADS, head_normal, make_inputs
+    prev = oracle.set_num_threads(1)
+    out = {}
+    try:
+        w1 = WORKLOADS["single_head_f32_n256_d64"]
+        x1 = make_inputs(w1)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.attention(x1["q"], x1["k"], x1["v"], w1.sm_scale, w1.causal)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 1.0:
+                break
+        out[w1.name] = {"gflops": round(w1.flops * reps / dt / 1e9, 3), "s_per_call": round(dt / reps, 5)}
+        w2 = WORKLOADS["gpt2_medium_bf16_n1024_d64"]
+        q, k, v = (torch.from_numpy(head_normal(w2.seed_id, t, 0, 0, w2.n_q, w2.d)).to(torch.bfloat16)
+                   for t in range(3))
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w2.sm_scale, w2.causal)
+        dt = time.perf_counter() - t0
+        f = 4.0 * w2.n_q * w2.n_kv * w2.d
+        out[w2.name + "_one_head"] = {"gflops": round(f / dt / 1e9, 3), "s": round(dt, 3)}
+    finally:
+        oracle.set_num_threads(prev)
+    return out
+
+
+def cpu_baseline(w, x, o_gpu=None, lse_gpu=None, target_s: float = 25.0):
+    """The fp64 oracle (as it stands) on the same workload: the whole workload
+    when it takes about target_s seconds or less of host time, else a uniform
+    row sample grown until one run takes about that long (the last run is
+    reported).  Returns (baseline record, parity record): the oracle's rows
+    are compared with the GPU's O and LSE (max abs, relative L2, LSE max
+    abs over the compared rows)."""
     import oracle
     rng = np.random.default_rng([w.seed_id, 7])
     total = w.B * w.H * w.n_q
@@ -126,30 +186,49 @@ def cpu_baseline(w, x, target_s: float = 15.0) -> dict:
         vis = np.minimum(i + 1, w.n_kv) if w.causal else np.full(rows.shape, w.n_kv)
         return float(np.sum(4.0 * vis * w.d))
 
-    qo, ko, vo = x["q"], x["k"], x["v"]
-    if w.dtype == "fp8_e4m3":
-        dq, dk, dv = x["descale"]
-        qo, ko, vo = (oracle.dequant_e4m3(t, s) for t, s in ((qo, dq), (ko, dk), (vo, dv)))
+    qo, ko, vo = oracle_operands(w, x)
     # grow the sample until it takes about target_s (the per-call fp64 conversion
     # of the touched heads is a fixed cost, so one calibration step undershoots)
     n = min(1024, total)
     while True:
-        rows = np.sort(rng.choice(total, size=n, replace=False))
+        rows = np.arange(total) if n == total else np.sort(rng.choice(total, size=n, replace=False))
         t0 = time.perf_counter()
-        oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
+        o_ref, lse_ref = oracle.attention(qo, ko, vo, w.sm_scale, w.causal, rows=rows)
         dt = time.perf_counter() - t0
         if dt >= 0.6 * target_s or n == total:
             break
         n = int(min(total, max(2 * n, n * target_s / max(dt, 1e-3))))
     f = flops_of(rows)
-    return {
+    whole = rows.size == total
+    base = {
         "value": round(f / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": "%d of %d query rows (uniform, without replacement) of workload %s; fp64 "
-                  "three-pass oracle, %.1f s, %.4g FLOP" % (rows.size, total, w.name, dt, f),
+        "cpu_model": cpu_model(),
+        "sample": "%s of workload %s (%d of %d query rows); fp64 three-pass oracle, %.1f s, %.4g FLOP"
+                  % ("the whole tensor" if whole else "a uniform row sample without replacement",
+                     w.name, rows.size, total, dt, f),
+        "one_thread": one_thread_timings(),
     }
+    parity = None
+    if o_gpu is not None:
+        import torch
+        sel = torch.from_numpy(rows).to(o_gpu.device)
+        og = o_gpu.reshape(-1, w.d)[sel].double().cpu().numpy()
+        diff = og - o_ref
+        parity = {"rows": int(rows.size), "whole_tensor": bool(whole),
+                  "max_abs": float(np.abs(diff).max()),
+                  "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(o_ref))}
+        if lse_gpu is not None:
+            lg = lse_gpu.reshape(-1)[sel].double().cpu().numpy()
+            parity["lse_max_abs"] = float(np.abs(lg - lse_ref).max())
+        bars = PARITY_BARS[w.dtype]
+        parity["bars"] = {"max_abs": bars[0], "rel_l2": bars[1], "lse_max_abs": bars[2]}
+        parity["within_bars"] = bool(
+            np.isfinite(og).all() and (bars[0] is None or parity["max_abs"] <= bars[0])
+            and parity["rel_l2"] <= bars[1] and parity.get("lse_max_abs", 0.0) <= bars[2])
+    return base, parity
 
 
 def cpu_baseline_bwd(w, x, dout, target_s: float = 15.0) -> dict:
@@ -719,7 +798,10 @@ def main(argv=None) -> int:
             rec["roofline"]["frac_of_measured_peak"] = round(
                 achieved / extras["device"]["mfma_tflops"], 4)
     if not args.no_cpu_baseline and args.dropout == 0.0:
-        rec["cpu_baseline"] = (cpu_baseline_bwd(w, x, do.cpu()) if args.bwd else cpu_baseline(w, x))
+        if args.bwd:
+            rec["cpu_baseline"] = cpu_baseline_bwd(w, x, do.cpu())
+        else:
+            rec["cpu_baseline"], rec["parity"] = cpu_baseline(w, x, o, lse)
     print(json.dumps(rec), flush=True)
     return 0
 

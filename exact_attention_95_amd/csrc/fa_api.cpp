@@ -78,7 +78,10 @@ int dropout_p8(float p) {
 
 }  // namespace
 
-extern "C" int fa_validate(const fa_fwd_args *a) {
+namespace {
+// Checks shared by the single-pass and split-KV forwards (everything but the
+// single-pass key-range limit).
+int validate_fwd_common(const fa_fwd_args *a) {
     if (!a) return FA_ERR_NULL;
     if (a->dtype < FA_F32 || a->dtype > FA_FP8_E4M3) return FA_ERR_DTYPE;
     if (a->d != 64 && a->d != 128 && a->d != 256) return FA_ERR_HEAD_DIM;
@@ -115,6 +118,16 @@ extern "C" int fa_validate(const fa_fwd_args *a) {
     if (lb && (overlap(a->LSE, lb, a->Q, qb) || overlap(a->LSE, lb, a->K, kb) ||
                overlap(a->LSE, lb, a->V, kb) || overlap(a->LSE, lb, a->O, ob)))
         return FA_ERR_ALIAS;
+    return FA_OK;
+}
+}  // namespace
+
+extern "C" int fa_validate(const fa_fwd_args *a) {
+    const int st = validate_fwd_common(a);
+    if (st != FA_OK) return st;
+    // the float32 running sums of one pass hold ordinary rounding up to this
+    // many keys per row (include/fa.h, "Very long key ranges")
+    if (a->N_kv > FA_MAX_NKV_SINGLE_PASS) return FA_ERR_LONG_KV;
     return FA_OK;
 }
 
@@ -154,6 +167,7 @@ extern "C" const char *fa_strerror(int status) {
         case FA_ERR_VARIANT: return "no compiled variant for this problem (or tile_override out of range)";
         case FA_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
         case FA_ERR_DROPOUT: return "dropout_p outside [0, 1), or dropout not supported here (fp16/bf16, d <= 128, not split-KV)";
+        case FA_ERR_LONG_KV: return "N_kv above the single-pass limit of 2^20 keys per row; use fa_fwd_splitkv";
         default: return "unknown status";
     }
 }
@@ -244,6 +258,7 @@ namespace {
 // Chunking of the key range for split-KV: chunks of a whole number of 64-key
 // tiles, none empty.  Returns the number of chunks and sets *kv_split.
 const int kSplitTile = 64, kSplitRows = 128;  // key tile and query block of the split kernels
+const int64_t kMaxChunkTiles = FA_MAX_NKV_SINGLE_PASS / kSplitTile;
 
 int plan_splits(const fa_fwd_args *a, int num_splits, int *kv_split) {
     const int64_t tiles = (a->N_kv + kSplitTile - 1) / kSplitTile;
@@ -257,6 +272,9 @@ int plan_splits(const fa_fwd_args *a, int num_splits, int *kv_split) {
     }
     if (want > tiles) want = tiles;
     if (want > 4096) want = 4096;
+    // no chunk longer than the single-pass limit (float32 running sums)
+    const int64_t min_chunks = (tiles + kMaxChunkTiles - 1) / kMaxChunkTiles;
+    if (want < min_chunks) want = min_chunks;
     if (want < 1) want = 1;
     const int64_t per = (tiles + want - 1) / want;
     *kv_split = (int)(per * kSplitTile);
@@ -267,13 +285,22 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // Status of the split-KV arguments before the workspace is looked at.
 int validate_split(const fa_fwd_args *a, int num_splits) {
-    const int st = fa_validate(a);
+    const int st = validate_fwd_common(a);
     if (st != FA_OK) return st;
     if (num_splits < 0) return FA_ERR_SHAPE;
     if (dropout_p8(a->dropout_p) != 0) return FA_ERR_DROPOUT;
     const int nv = count_variants(a->dtype, a->d, a->causal, 1);
     if (nv == 0) return FA_ERR_VARIANT;
     if (a->tile_override > nv) return FA_ERR_VARIANT;
+    if (a->B * a->H == 0 || a->N_q == 0) return FA_OK;
+    // the grid (chunks x heads x query blocks) must fit 2^31 - 1 workgroups,
+    // and the float32 partials (chunks x rows x (d + 1) x 4 bytes) int64
+    int kv_split = 0;
+    const int64_t n = plan_splits(a, num_splits, &kv_split);
+    const int64_t blocks = a->B * a->H * ((a->N_q + kSplitRows - 1) / kSplitRows);
+    if (blocks > INT32_MAX / n) return FA_ERR_SHAPE;
+    const int64_t rows = a->B * a->H * a->N_q;
+    if (rows > INT64_MAX / 8 / n / (a->d + 1)) return FA_ERR_SHAPE;
     return FA_OK;
 }
 

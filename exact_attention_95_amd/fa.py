@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_SCALE,
- FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE, FA_ERR_DROPOUT) = range(13)
+ FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE, FA_ERR_DROPOUT,
+ FA_ERR_LONG_KV) = range(14)
+FA_MAX_NKV_SINGLE_PASS = 1 << 20  # include/fa.h
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
             "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_bwd",
@@ -212,6 +214,67 @@ def make_args(q, k, v, o, lse, scale: float, causal: bool, descale=(1.0, 1.0, 1.
     return a
 
 
+def check_tensors(q, k, v, out=None, lse=None, extra=(), workspace=None, need_cuda: bool = True,
+                  dtypes=None, out_dtype=None):
+    """Host-side checks of the torch tensors handed to the library, before any
+    launch: q [B,H,N_q,d] and k, v [B,H,N_kv,d] of one dtype (``dtypes``: the
+    allowed ones); ``out`` [B,H,N_q,d] of ``out_dtype``; ``lse`` float32
+    [B,H,N_q]; ``extra``: (name, tensor, shape, dtype) tuples; ``workspace``
+    uint8.  Every tensor must be contiguous and on q's device (a GPU device
+    unless ``need_cuda`` is False).  Raises TypeError (dtype) or ValueError
+    (anything else); the C library checks sizes, alignment and overlap again
+    from the raw arguments."""
+    import torch
+    named = [("q", q), ("k", k), ("v", v)]
+    if need_cuda and not all(t.is_cuda for _, t in named):
+        raise RuntimeError("the attention library needs GPU tensors; there is no CPU path")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected [B,H,N,d] tensors: q %s k %s v %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype (got %s, %s, %s)" % (q.dtype, k.dtype, v.dtype))
+    if dtypes is not None and q.dtype not in dtypes:
+        raise TypeError("unsupported dtype %s here" % q.dtype)
+    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                              tuple(v.shape)))
+    B, H, N_q, d = q.shape
+    if out is not None:
+        named.append(("out", out))
+        if tuple(out.shape) != (B, H, N_q, d):
+            raise ValueError("out must be [B,H,N_q,d] = %s, got %s" % ((B, H, N_q, d), tuple(out.shape)))
+        if out_dtype is not None and out.dtype != out_dtype:
+            raise TypeError("out must be %s, got %s" % (out_dtype, out.dtype))
+    if lse is not None:
+        named.append(("lse", lse))
+        if tuple(lse.shape) != (B, H, N_q):
+            raise ValueError("lse must be [B,H,N_q] = %s, got %s" % ((B, H, N_q), tuple(lse.shape)))
+        if lse.dtype != torch.float32:
+            raise TypeError("lse must be float32, got %s" % lse.dtype)
+    for name, t, shape, dt in extra:
+        named.append((name, t))
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s must be %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+        if t.dtype != dt:
+            raise TypeError("%s must be %s, got %s" % (name, dt, t.dtype))
+    if workspace is not None:
+        named.append(("workspace", workspace))
+        if workspace.dtype != torch.uint8:
+            raise TypeError("workspace must be uint8, got %s" % workspace.dtype)
+    for name, t in named:
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.device != q.device:
+            raise ValueError("%s is on %s, q on %s" % (name, t.device, q.device))
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
 def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None, out=None,
         lse=None, with_lse: bool = True, stream=None, tile: int = 0, dropout_p: float = 0.0,
         seed: int = 0, offset: int = 0):
@@ -220,35 +283,22 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None,
     q: [B,H,N_q,d]; k, v: [B,H,N_kv,d]; all contiguous, same dtype, on one
     gfx950 device.  scale defaults to 1/sqrt(d) (as float32).  For
     float8_e4m3fn inputs, descale = (descale_q, descale_k, descale_v) and O is
-    bfloat16.  ``stream``: a torch stream or raw hipStream_t (default: torch's
+    bfloat16.  ``out`` / ``lse``: optional preallocated outputs (checked).
+    ``stream``: a torch stream or raw hipStream_t (default: torch's
     current stream).  ``dropout_p``, ``seed``, ``offset``: dropout of P with
     the library's Philox mask (see include/fa.h).
     """
     import torch
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise RuntimeError("fa.fwd needs GPU tensors; there is no CPU path")
-    if q.dtype != k.dtype or q.dtype != v.dtype:
-        raise TypeError("q, k, v must share a dtype")
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("expected [B,H,N,d] tensors")
-    if k.shape != v.shape or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
-        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
-                                                              tuple(v.shape)))
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
+    out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    check_tensors(q, k, v, out, lse, out_dtype=out_dtype)
     B, H, N_q, d = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
-    out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if out is None:
         out = torch.empty((B, H, N_q, d), dtype=out_dtype, device=q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q.device)
     args = make_args(q, k, v, out, lse, scale, causal, descale or (1.0, 1.0, 1.0), stream, tile,
                      (dropout_p, seed, offset))
     with torch.cuda.device(q.device):
@@ -269,8 +319,8 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
     device tensor) is given.
     """
     import torch
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
-        raise RuntimeError("fa.fwd_splitkv needs GPU tensors; there is no CPU path")
+    check_tensors(q, k, v, out, lse, workspace=workspace, dtypes=(torch.bfloat16, torch.float16),
+                  out_dtype=q.dtype)
     B, H, N_q, d = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
@@ -278,10 +328,7 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
         out = torch.empty((B, H, N_q, d), dtype=q.dtype, device=q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q.device)
     args = make_args(q, k, v, out, lse, scale, causal, (1.0, 1.0, 1.0), stream, tile)
     need = fa_splitkv_workspace_bytes(args, num_splits)
     if need < 0:
@@ -326,23 +373,15 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, s
     tensor) is given.
     """
     import torch
-    for t in (q, k, v, o, lse, do):
-        if not t.is_cuda:
-            raise RuntimeError("fa.bwd needs GPU tensors; there is no CPU path")
-        if not t.is_contiguous():
-            raise ValueError("inputs must be contiguous")
-    if len({q.dtype, k.dtype, v.dtype, o.dtype, do.dtype}) != 1:
-        raise TypeError("q, k, v, o, do must share a dtype")
-    if o.shape != q.shape or do.shape != q.shape or lse.shape != q.shape[:3] or k.shape != v.shape:
-        raise ValueError("shape mismatch")
+    B, H, N_q, d = q.shape if q.dim() == 4 else (0, 0, 0, 0)
+    check_tensors(q, k, v, dtypes=(torch.bfloat16, torch.float16), workspace=workspace,
+                  extra=(("o", o, (B, H, N_q, d), q.dtype), ("do", do, (B, H, N_q, d), q.dtype),
+                         ("lse", lse, (B, H, N_q), torch.float32)))
     B, H, N_q, d = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    stream = _stream_handle(stream, q.device)
     args = make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream,
                          (dropout_p, seed, offset))
     need = fa_bwd_workspace_bytes(args)
@@ -362,8 +401,7 @@ def dropout_mask(dropout_p: float, seed: int, offset: int, B: int, H: int, N_q: 
     """The dropout keep mask ([B,H,N_q,N_kv] uint8 on the GPU) the kernels use."""
     import torch
     m = torch.empty((B, H, N_q, N_kv), dtype=torch.uint8, device=device)
-    if stream is None:
-        stream = torch.cuda.current_stream(m.device).cuda_stream
+    stream = _stream_handle(stream, m.device)
     with torch.cuda.device(m.device):
         st = fa_dropout_mask(dropout_p, seed, offset, B * H, N_q, N_kv, m.data_ptr() if m.numel() else None,
                              stream)

@@ -13,16 +13,20 @@
  * computed tile by tile with the online softmax, so S and P never reach HBM.
  * The result equals the definition up to floating-point rounding.
  *
- * Very long key ranges.  The single-pass forward adds each key tile's share
- * to float32 running sums per row (the row sum and the output accumulator),
- * once per tile.  When much of a row's softmax mass is spread thinly over a
- * very long key range, each addition rounds away a part of a small addend,
- * and the error grows with the number of tiles: with 2^24 keys of which the
- * low-score majority carries 2-12 % of the mass, O is off by about 1e-2 and
- * LSE by about 6e-3.  fa_fwd_splitkv sums short chunks and merges them, and
- * stays at ordinary rounding there (O relative L2 2e-3, LSE 2e-5 measured);
- * use it for key ranges of millions of keys.  Byte offsets are 64-bit
- * throughout: tensors larger than 4 GiB are supported.
+ * Very long key ranges.  The single-pass forward (fa_fwd, fa_fwd_ex) adds
+ * each key tile's share to float32 running sums per row (the row sum once
+ * per tile, the output accumulator once per 16 to 64 keys).  Each addition
+ * can round away up to half an ulp of the running sum, so when much of a
+ * row's softmax mass is spread thinly over a long key range the error grows
+ * with the number of additions: with 2^24 keys of which the low-score
+ * majority carries 2-12 % of the mass, O is off by about 1e-2 and LSE by
+ * about 6e-3, against bars of 5e-3 and 1e-3.  The single-pass entry points
+ * therefore accept at most FA_MAX_NKV_SINGLE_PASS = 2^20 keys per row, where
+ * the same worst case stays at ordinary rounding, and return FA_ERR_LONG_KV
+ * beyond it.  fa_fwd_splitkv sums chunks of at most 2^20 keys and merges
+ * them, and handles any N_kv up to 2^30 (O relative L2 2e-3, LSE 2e-5
+ * measured at 2^24 keys).  Byte offsets are 64-bit throughout: tensors
+ * larger than 4 GiB are supported.
  *
  * Layout.  Q is [B, H, N_q, d]; K and V are [B, H, N_kv, d]; O is
  * [B, H, N_q, d]; LSE is [B, H, N_q].  All are dense row-major with d the
@@ -77,15 +81,21 @@ typedef enum {
     FA_ERR_LAUNCH = 9,    /* the kernel launch failed */
     FA_ERR_VARIANT = 10,  /* no compiled variant for this problem / tile_override out of range */
     FA_ERR_WORKSPACE = 11, /* split-KV or backward workspace NULL, misaligned or too small */
-    FA_ERR_DROPOUT = 12    /* dropout_p outside [0, 1), or dropout where it is not supported */
+    FA_ERR_DROPOUT = 12,   /* dropout_p outside [0, 1), or dropout where it is not supported */
+    FA_ERR_LONG_KV = 13    /* N_kv above FA_MAX_NKV_SINGLE_PASS for fa_fwd / fa_fwd_ex */
 } fa_status;
+
+/* Longest key range per row the single-pass forward accepts (see "Very
+ * long key ranges"); also the longest chunk fa_fwd_splitkv forms. */
+#define FA_MAX_NKV_SINGLE_PASS (1 << 20)
 
 /*
  * fa_fwd -- attention forward on the null stream.
  *
  * Q, K, V: device inputs (see Layout); O: device output; LSE: device
  * float32 output, or NULL to skip it.  B, H >= 0 batches and heads;
- * N_q >= 0 query rows and N_kv >= 1 key rows per head; d in {64, 128, 256}.
+ * N_q >= 0 query rows and 1 <= N_kv <= FA_MAX_NKV_SINGLE_PASS key rows per
+ * head (FA_ERR_LONG_KV above it); d in {64, 128, 256}.
  * B, H or N_q equal to 0 is a successful no-op.  scale multiplies QK^T
  * before the softmax (1/sqrt(d) in the pages); any finite value is valid,
  * including 0 and negative values.  causal: 0 or non-zero (see Causal
@@ -159,10 +169,14 @@ int fa_validate(const fa_fwd_args *args);
  * when fa_fwd_ex's workgroups (B * H * ceil(N_q / 256) at d = 128) cannot fill
  * the GPU (few query rows, long key ranges).
  *
- * args: as for fa_fwd_ex; dtype FA_BF16 or FA_F16 and d in {64, 128}
- * (otherwise FA_ERR_VARIANT); tile_override 0 or 1.  num_splits: 0 lets the
- * library choose, otherwise an upper bound (every chunk is non-empty, so
- * fewer may be used).  workspace: device memory owned by the caller, 256-byte
+ * args: as for fa_fwd_ex, except that N_kv may exceed
+ * FA_MAX_NKV_SINGLE_PASS (up to 2^30); dtype FA_BF16 or FA_F16 and d in
+ * {64, 128} (otherwise FA_ERR_VARIANT); tile_override 0 or 1.  num_splits:
+ * 0 lets the library choose, otherwise an upper bound (every chunk is
+ * non-empty, so fewer may be used), except that no chunk is made longer
+ * than FA_MAX_NKV_SINGLE_PASS keys: more chunks are used where needed.
+ * FA_ERR_SHAPE if num_splits < 0 or the grid (chunks x B x H x query
+ * blocks of 128 rows) exceeds 2^31 - 1 workgroups.  workspace: device memory owned by the caller, 256-byte
  * aligned, at least fa_splitkv_workspace_bytes(args, num_splits) bytes, not
  * overlapping Q, K, V, O or LSE (FA_ERR_WORKSPACE / FA_ERR_ALIAS otherwise);
  * its contents are overwritten.  Both kernels run on args->stream, in order.

@@ -108,6 +108,8 @@ def _declare(lib):
     lib.fa_oracle_merge.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dp, _dp]
     lib.fa_oracle_num_threads.restype = ctypes.c_int
     lib.fa_oracle_num_threads.argtypes = []
+    lib.fa_oracle_set_num_threads.restype = ctypes.c_int
+    lib.fa_oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.fa_oracle_e4m3_to_double.restype = ctypes.c_double
     lib.fa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
     lib.fa_oracle_dequant_e4m3.restype = ctypes.c_int
@@ -203,6 +205,11 @@ def attention(q, k, v, scale: float, causal: bool = False, rows=None,
 def num_threads(lib=None) -> int:
     """Threads the oracle's parallel loops use (OpenMP)."""
     return int((lib or load()).fa_oracle_num_threads())
+
+
+def set_num_threads(n: int, lib=None) -> int:
+    """Sets the threads of later parallel loops on this thread; returns the previous count."""
+    return int((lib or load()).fa_oracle_set_num_threads(int(n)))
 
 
 def cuts_from_block(n: int, block: int) -> np.ndarray:

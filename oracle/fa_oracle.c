@@ -54,6 +54,20 @@ int fa_oracle_num_threads(void)
 #endif
 }
 
+/* Sets the number of threads later parallel regions of the calling thread
+ * use (n >= 1); returns the previous value.  Used to time the oracle on one
+ * core beside its multi-core run. */
+int fa_oracle_set_num_threads(int n)
+{
+    const int prev = fa_oracle_num_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}
+
 /* Number of keys row i may attend to. */
 static int64_t visible_keys(int64_t i, int64_t n_kv, int causal)
 {

@@ -139,10 +139,61 @@ def test_validate_null_args_pointer():
     assert lib.fa_fwd_ex(None) == fa.FA_ERR_NULL
 
 
+def declared_statuses(header=HEADER):
+    """(name, value) of every fa_status enumerator the header declares."""
+    text = open(header).read()
+    body = text[text.index("FA_OK = 0"):text.index("} fa_status;")]
+    return [(n, int(v)) for n, v in re.findall(r"(FA_\w+)\s*=\s*(\d+)", body)]
+
+
 def test_strerror_names_every_status():
-    msgs = {fa.fa_strerror(s) for s in range(11)}
-    assert len(msgs) == 11
+    statuses = declared_statuses()
+    assert [v for _, v in statuses] == list(range(len(statuses)))  # dense, from 0
+    assert len(statuses) == 14
+    for name, value in statuses:
+        assert getattr(fa, name) == value, name  # the binding mirrors the header
+    msgs = {fa.fa_strerror(v) for _, v in statuses}
+    assert len(msgs) == len(statuses) and "unknown status" not in msgs
+    assert fa.fa_strerror(len(statuses)) == "unknown status"
     assert fa.fa_strerror(12345) == "unknown status"
+    assert fa.fa_strerror(-1) == "unknown status"
+
+
+def test_single_pass_key_range_limit():
+    """fa_fwd / fa_fwd_ex accept at most FA_MAX_NKV_SINGLE_PASS keys per row;
+    split-KV takes longer rows (chunks of at most that many keys)."""
+    text = open(HEADER).read()
+    assert re.search(r"#define FA_MAX_NKV_SINGLE_PASS \(1 << 20\)", text)
+    assert fa.FA_MAX_NKV_SINGLE_PASS == 1 << 20
+    big = dict(B=1, H=1, N_q=3, d=128, Q=0x1000, K=1 << 32, V=1 << 34, O=0x2000, LSE=0x3000)
+    lim = fa.FA_MAX_NKV_SINGLE_PASS
+    assert fa.fa_validate(good_args(N_kv=lim, **big)) == fa.FA_OK
+    assert fa.fa_validate(good_args(N_kv=lim + 1, **big)) == fa.FA_ERR_LONG_KV
+    for dt in (fa.FA_F32, fa.FA_F16, fa.FA_FP8_E4M3):
+        assert fa.fa_validate(good_args(N_kv=lim + 1, dtype=dt, **big)) == fa.FA_ERR_LONG_KV
+    a = good_args(N_kv=lim + 1, **big)
+    assert fa.fa_fwd_ex(a) == fa.FA_ERR_LONG_KV        # refused before any HIP call
+    lib = fa.load()
+    assert lib.fa_fwd(a.Q, a.K, a.V, a.O, a.LSE, 1, 1, 3, lim + 1, 128, 0.1, 0, fa.FA_BF16) == \
+        fa.FA_ERR_LONG_KV
+    # split-KV: any N_kv up to 2^30; even num_splits = 1 is cut into chunks of <= 2^20 keys
+    n_kv = (1 << 24) + 37
+    a = good_args(N_kv=n_kv, **big)
+    chunks = -(-n_kv // lim)
+    one = fa.fa_splitkv_workspace_bytes(a, 1)
+    want = -(-chunks * 3 * 128 * 4 // 256) * 256 + -(-chunks * 3 * 4 // 256) * 256
+    assert one == want
+    assert fa.fa_splitkv_workspace_bytes(good_args(N_kv=(1 << 30) + 1, **big), 0) == -1
+
+
+def test_splitkv_grid_bound():
+    """The split-KV grid (chunks x heads x 128-row query blocks) must fit 2^31 - 1."""
+    # 2^22 heads of 1024 rows: 8 query blocks each, 2^25 blocks; 64 chunks would be 2^31
+    a = good_args(B=1 << 11, H=1 << 11, N_q=1024, N_kv=64 * 64, d=64, K=1 << 44, V=1 << 45,
+                  O=1 << 46, LSE=1 << 47, Q=1 << 43)
+    assert fa.fa_splitkv_workspace_bytes(a, 63) > 0
+    assert fa.fa_splitkv_workspace_bytes(a, 64) == -1
+    assert fa.fa_fwd_splitkv(a, 64, 1 << 48, 1 << 50) == fa.FA_ERR_SHAPE
 
 
 def test_variant_table():
@@ -310,3 +361,48 @@ def test_dropout_mask_entry_validation():
     assert fa.fa_dropout_mask(0.1, 1, 2, 0, 4, 4, None) == fa.FA_OK
     assert fa.fa_dropout_mask(0.1, 1, 2, 3, 0, 4, None) == fa.FA_OK
     assert fa.fa_dropout_mask(0.1, 1, 2, 1, 4, 4, None) == fa.FA_ERR_NULL
+
+
+def test_tensor_checks_run_before_any_launch():
+    """The Python binding rejects mismatched dtypes, shapes, non-contiguous or
+    misplaced tensors (including out, lse and the workspace) on the host; the
+    checker runs on CPU tensors here with the device requirement lifted."""
+    import torch
+    chk = fa.check_tensors
+    bf, f16 = torch.bfloat16, torch.float16
+    q = torch.zeros(2, 3, 5, 64, dtype=bf)
+    k = torch.zeros(2, 3, 7, 64, dtype=bf)
+    chk(q, k, k, need_cuda=False)
+    chk(q, k, k, torch.zeros(2, 3, 5, 64, dtype=bf), torch.zeros(2, 3, 5), need_cuda=False, out_dtype=bf)
+    bad = [
+        (TypeError, dict(k=k.to(torch.float8_e4m3fn))),
+        (TypeError, dict(v=k.to(f16))),
+        (ValueError, dict(k=torch.zeros(2, 3, 7, 128, dtype=bf), v=torch.zeros(2, 3, 7, 128, dtype=bf))),
+        (ValueError, dict(v=torch.zeros(2, 3, 8, 64, dtype=bf))),
+        (ValueError, dict(k=torch.zeros(2, 3, 64, 7, dtype=bf).transpose(2, 3))),
+        (ValueError, dict(q=torch.zeros(3, 5, 64, dtype=bf))),
+        (ValueError, dict(out=torch.zeros(2, 3, 4, 64, dtype=bf))),
+        (ValueError, dict(out=torch.zeros(2, 3, 64, 5, dtype=bf).transpose(2, 3))),
+        (TypeError, dict(out=torch.zeros(2, 3, 5, 64, dtype=f16))),
+        (TypeError, dict(lse=torch.zeros(2, 3, 5, dtype=bf))),
+        (ValueError, dict(lse=torch.zeros(2, 3, 4))),
+        (TypeError, dict(workspace=torch.zeros(64, dtype=torch.float32))),
+        (ValueError, dict(workspace=torch.zeros(64, 2, dtype=torch.uint8)[:, 0])),
+        (TypeError, dict(dtypes=(f16,))),
+    ]
+    for exc, kw in bad:
+        args = dict(q=q, k=k, v=k, out=None, lse=None, workspace=None, out_dtype=bf)
+        args.update(kw)
+        with pytest.raises(exc):
+            chk(args.pop("q"), args.pop("k"), args.pop("v"), need_cuda=False, **args)
+    # backward extras: o, do [B,H,N_q,d] in q's dtype and float32 lse
+    ok = (("o", q, (2, 3, 5, 64), bf), ("lse", torch.zeros(2, 3, 5), (2, 3, 5), torch.float32))
+    chk(q, k, k, extra=ok, need_cuda=False)
+    with pytest.raises(TypeError):
+        chk(q, k, k, extra=(("lse", torch.zeros(2, 3, 5, dtype=bf), (2, 3, 5), torch.float32),),
+            need_cuda=False)
+    with pytest.raises(ValueError):
+        chk(q, k, k, extra=(("do", q[:, :, :4], (2, 3, 5, 64), bf),), need_cuda=False)
+    # every public entry point refuses CPU tensors before touching the library's kernels
+    with pytest.raises(RuntimeError, match="GPU"):
+        fa.fwd_splitkv(q, k, k)

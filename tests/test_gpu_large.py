@@ -10,11 +10,13 @@ where a 32-bit offset would wrap.
   768, 2 GiB + 1280, 4 GiB - 256, 4 GiB and the last row, whose large scores
   carry the softmax mass (each dominates some rows).  O and LSE then have an
   exact closed form (plain softmax attention evaluated in fp64 over the five
-  specials plus n_zero equal keys).  With scores of about 39 the zero keys'
-  share is below 1e-8 and both entry points must match; with scores of about
-  18 the zero keys carry 2-12 % spread over 2^24 keys, which the single-pass
-  kernel's float32 running sums cannot hold to the bar (see the test), and
-  the split-KV entry point must match.
+  specials plus n_zero equal keys).  The single-pass entry point refuses rows
+  past 2^20 keys (FA_ERR_LONG_KV); split-KV must match both with scores of
+  about 39 (zero keys below 1e-8 of the mass) and with scores of about 18
+  (zero keys carrying 2-12 % spread over 2^24 keys).
+- The same long-tail case at 2^20 keys, the single-pass limit: both entry
+  points must match.  Nine heads of 2^20 keys at d = 256 put specials past
+  the 4 GiB offset for the single-pass kernel.
 - Queries past 4 GiB: two heads of 2^24 + 2^22 + 3 queries (Q and O 5 GiB
   each), with sampled rows around the 2 GiB and 4 GiB offsets checked against
   the fp64 oracle, with and without the causal mask; and the same with E4M3
@@ -60,79 +62,133 @@ def check(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, label: str):
     assert err["lse_max_abs"] <= LSE_TOL, (label, err)
 
 
-def keys_past_4gib_case(big: float):
-    """One head of 2^24 + 37 keys: zero rows with V = 1/4, and five special
-    keys whose first component is `big` (Q's first component is 1), at byte
-    offsets 768, 2 GiB + 1280, 4 GiB - 256, 4 GiB and the last row.  Returns
-    the device tensors, the scale, and O, LSE and the zero keys' share of the
-    softmax mass in closed form (fp64)."""
-    n_q, n_kv, d = 33, (1 << 24) + 37, 128
-    require_device_bytes(2 * n_kv * d * 2)
+def sparse_keys_case(H: int, n_kv: int, d: int, specials, big: float, seed: int = 95, n_q: int = 33):
+    """H heads of n_kv keys: zero rows with V = 1/4, except the `specials`
+    ((head, row) pairs, at least one per head), whose first component is
+    `big` (Q's first component is 1).  Returns the device tensors, the scale,
+    and per head O, LSE and the zero keys' share of the softmax mass in
+    closed form (fp64): plain softmax attention over the head's specials plus
+    n_zero equal keys of score 0."""
+    require_device_bytes(2 * H * n_kv * d * 2)
     scale = float(np.float32(1.0 / math.sqrt(d)))
-    g = torch.Generator().manual_seed(95)
-    q = torch.randn(n_q, d, generator=g)
-    q[:, 0] = 1.0
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(H, n_q, d, generator=g)
+    q[:, :, 0] = 1.0
     q = q.to(torch.bfloat16)
-    special = [3, (1 << 23) + 5, (1 << 24) - 1, 1 << 24, n_kv - 1]
-    ks = torch.randn(len(special), d, generator=g)
+    ks = torch.randn(len(specials), d, generator=g)
     ks[:, 0] = big  # the random part of the score decides which special dominates a row
     ks = ks.to(torch.bfloat16)
-    vs = torch.randn(len(special), d, generator=g).to(torch.bfloat16)
+    vs = torch.randn(len(specials), d, generator=g).to(torch.bfloat16)
     v_zero = 0.25
-    say("keys past 4 GiB: n_kv", n_kv, "special rows", special, "big", big)
-    k = torch.zeros(1, 1, n_kv, d, dtype=torch.bfloat16, device="cuda")
-    v = torch.full((1, 1, n_kv, d), v_zero, dtype=torch.bfloat16, device="cuda")
-    idx = torch.tensor(special, device="cuda")
-    k[0, 0, idx] = ks.cuda()
-    v[0, 0, idx] = vs.cuda()
+    k = torch.zeros(1, H, n_kv, d, dtype=torch.bfloat16, device="cuda")
+    v = torch.full((1, H, n_kv, d), v_zero, dtype=torch.bfloat16, device="cuda")
+    hs = torch.tensor([h for h, _ in specials], device="cuda")
+    rs = torch.tensor([r for _, r in specials], device="cuda")
+    k[0, hs, rs] = ks.cuda()
+    v[0, hs, rs] = vs.cuda()
 
-    # closed form in fp64: the specials' scores, and n_zero keys of score 0, value v_zero
-    q64, k64, v64 = q.double().numpy(), ks.double().numpy(), vs.double().numpy()
-    s = scale * (q64 @ k64.T)                                   # [n_q, 5]
-    n_zero = n_kv - len(special)
-    m = np.maximum(s.max(axis=1), 0.0)
-    w = np.exp(s - m[:, None])
-    w0 = n_zero * np.exp(-m)
-    ell = w0 + w.sum(axis=1)
-    o_ref = (w0[:, None] * v_zero + w @ v64) / ell[:, None]
-    lse_ref = m + np.log(ell)
-    # each special matters: reading any one of them wrong (here: as a zero row)
-    # moves O by far more than the tolerance
-    for j in range(len(special)):
-        w_drop = w.copy()
-        w_drop[:, j] = 0.0
-        w0_drop = w0 + np.exp(-m)
-        o_drop = (w0_drop[:, None] * v_zero + w_drop @ v64) / (w0_drop + w_drop.sum(axis=1))[:, None]
-        assert np.abs(o_drop - o_ref).max() > 0.5
-    return q.cuda()[None, None], k, v, scale, o_ref, lse_ref, w0 / ell
+    o_ref = np.empty((H, n_q, d))
+    lse_ref = np.empty((H, n_q))
+    tail = np.empty((H, n_q))
+    for h in range(H):
+        sel = [i for i, (hh, _) in enumerate(specials) if hh == h]
+        assert sel, "every head needs a special key"
+        q64 = q[h].double().numpy()
+        k64, v64 = ks[sel].double().numpy(), vs[sel].double().numpy()
+        s = scale * (q64 @ k64.T)                                   # [n_q, specials of h]
+        n_zero = n_kv - len(sel)
+        m = np.maximum(s.max(axis=1), 0.0)
+        w = np.exp(s - m[:, None])
+        w0 = n_zero * np.exp(-m)
+        ell = w0 + w.sum(axis=1)
+        o_ref[h] = (w0[:, None] * v_zero + w @ v64) / ell[:, None]
+        lse_ref[h] = m + np.log(ell)
+        tail[h] = w0 / ell
+        # each special matters: reading any one of them wrong (here: as a zero
+        # row) moves O by far more than the tolerance
+        for j in range(len(sel)):
+            w_drop = w.copy()
+            w_drop[:, j] = 0.0
+            w0_drop = w0 + np.exp(-m)
+            o_drop = (w0_drop[:, None] * v_zero + w_drop @ v64) / (w0_drop + w_drop.sum(axis=1))[:, None]
+            assert np.abs(o_drop - o_ref[h]).max() > 0.5
+    return q.cuda()[None], k, v, scale, o_ref, lse_ref, tail
+
+
+def keys_past_4gib_case(big: float):
+    """One head of 2^24 + 37 keys (K and V 4 GiB each); five special keys at
+    byte offsets 768, 2 GiB + 1280, 4 GiB - 256, 4 GiB and the last row."""
+    n_kv, d = (1 << 24) + 37, 128
+    special = [3, (1 << 23) + 5, (1 << 24) - 1, 1 << 24, n_kv - 1]
+    say("keys past 4 GiB: n_kv", n_kv, "special rows", special, "big", big)
+    return sparse_keys_case(1, n_kv, d, [(0, r) for r in special], big)
 
 
 def test_keys_past_4gib_closed_form():
     # scores about 39: the 2^24 zero-score keys carry under 1e-8 of the mass,
     # so the result depends on the five specials being read from the right
-    # addresses, not on how the long tail is summed
+    # addresses, not on how the long tail is summed.  The single-pass entry
+    # point refuses rows past 2^20 keys before any launch.
     q, k, v, scale, o_ref, lse_ref, tail = keys_past_4gib_case(440.0)
     assert tail.max() < 1e-8
-    o, lse = fa.fwd(q, k, v, scale=scale)
-    torch.cuda.synchronize()
-    check(o, lse, o_ref, lse_ref, "bf16", "single pass")
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, k, v, scale=scale)
+    assert e.value.status == fa.FA_ERR_LONG_KV
     o, lse = fa.fwd_splitkv(q, k, v, scale=scale)
     torch.cuda.synchronize()
     check(o, lse, o_ref, lse_ref, "bf16", "split-KV")
+    o, lse = fa.fwd_splitkv(q, k, v, scale=scale, num_splits=1)  # still cut into <= 2^20-key chunks
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "split-KV, num_splits=1")
 
 
 def test_long_tail_over_2_24_keys_split_kv():
     # scores about 18: the zero-score keys carry 2-12 % of the mass, spread
-    # over 2^24 keys.  The single-pass kernel adds each 64-key tile's share to
-    # one float32 running sum per row, 2^18 times, and each addition rounds
-    # away a fixed part of a small addend (here about 2 ulps of the sum), so
-    # its error grows with the number of key tiles; split-KV sums short
-    # chunks and merges them, and meets the bar.
+    # over 2^24 keys.  One float32 running sum over all 2^18 key tiles of a
+    # row would round away a fixed part of each small addend (here about 2
+    # ulps of the sum), an error that grows with the number of tiles; the
+    # single-pass entry point therefore refuses the case (FA_ERR_LONG_KV),
+    # and split-KV sums chunks of at most 2^20 keys and merges them.
     q, k, v, scale, o_ref, lse_ref, tail = keys_past_4gib_case(200.0)
     assert tail.max() > 1e-2 and tail.min() < 0.5
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, k, v, scale=scale)
+    assert e.value.status == fa.FA_ERR_LONG_KV
     o, lse = fa.fwd_splitkv(q, k, v, scale=scale)
     torch.cuda.synchronize()
     check(o, lse, o_ref, lse_ref, "bf16", "split-KV, long tail")
+
+
+def test_long_tail_at_the_single_pass_limit():
+    # the same worst case (identical small addends, a few % of the mass) at
+    # the longest key range the single-pass entry point accepts: 2^20 keys
+    n_kv, d = fa.FA_MAX_NKV_SINGLE_PASS, 128
+    special = [0, 7, 1 << 19, n_kv - 2, n_kv - 1]
+    q, k, v, scale, o_ref, lse_ref, tail = sparse_keys_case(1, n_kv, d, [(0, r) for r in special], 169.0)
+    say("long tail at 2^20 keys: tail share %.3g .. %.3g" % (tail.min(), tail.max()))
+    assert tail.max() > 1e-2 and tail.min() < 0.5
+    o, lse = fa.fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "single pass, long tail at the limit")
+    o, lse = fa.fwd_splitkv(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "split-KV, long tail at the limit")
+
+
+def test_single_pass_keys_past_4gib_across_heads():
+    # nine heads of 2^20 keys at d = 256 (512-byte rows): K and V 4.5 GiB
+    # each, head 8 starting at 4 GiB; specials in every head, several at byte
+    # offsets past 2 and 4 GiB, scores about 39 (zero keys under 1e-8 of the mass)
+    H, n_kv, d = 9, fa.FA_MAX_NKV_SINGLE_PASS, 256
+    specials = [(h, r) for h in range(H) for r in ((h * 7919) % n_kv, n_kv - 1 - h)]
+    specials += [(8, 3), (7, (1 << 19) + 1)]
+    q, k, v, scale, o_ref, lse_ref, tail = sparse_keys_case(H, n_kv, d, specials, 620.0)
+    assert tail.max() < 1e-8
+    say("heads past 4 GiB: last special at byte offset %.2f GiB"
+        % (max((h * n_kv + r) * d * 2 for h, r in specials) / GIB))
+    o, lse = fa.fwd(q, k, v, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, o_ref, lse_ref, "bf16", "single pass, heads past 4 GiB")
 
 
 @pytest.mark.parametrize("causal", [False, True])

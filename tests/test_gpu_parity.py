@@ -14,7 +14,8 @@ import torch
 from conftest import gpu_available
 from exact_attention_95_amd import fa
 from exact_attention_95_amd.inputs import WORKLOADS, make_inputs, random_problem
-from parity import LSE_TOL, TOL, assert_within, full_parity, run_gpu, sampled_parity, say
+from parity import (LSE_TOL, TOL, assert_within, default_rows, full_parity, run_gpu, sampled_parity,
+                    say, whole_parity)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -170,24 +171,116 @@ def test_validation_errors_reach_python():
     assert e.value.status == fa.FA_ERR_ALIAS
 
 
-# ---- full workload sizes, sampled rows, default launch configuration ----
+# ---- full workload sizes, default launch configuration ----
 
-FULL = [
-    ("gpt2_medium_bf16_n1024_d64", 256),
-    ("long_f16_causal_n4096_d64", 256),
-    ("long_f16_causal_n16384_d64", 256),
-    ("long_f16_causal_n65536_d64", 256),
-    ("headline_bf16_n8192_d128", 256),
-    ("headline_bf16_causal_n8192_d128", 256),
-    ("large_head_bf16_n16384_d256", 128),
-    ("fp8_e4m3_n16384_d128", 256),
+# Whole tensors against the oracle, streamed one head at a time (the oracle
+# takes seconds to about a minute and a half per workload on the host's cores).
+WHOLE = [
+    "gpt2_medium_bf16_n1024_d64",
+    "long_f16_causal_n4096_d64",
+    "long_f16_causal_n16384_d64",
+    "headline_bf16_n8192_d128",
+    "headline_bf16_causal_n8192_d128",
+    "large_head_bf16_n16384_d256",
+    "fp8_e4m3_n16384_d128",
 ]
 
 
-@pytest.mark.parametrize("name,br", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_rows(name, br):
+@pytest.mark.slow
+@pytest.mark.parametrize("name", WHOLE)
+def test_full_size_whole_tensor(name):
     w = WORKLOADS[name]
-    say("workload", w)
+    say("workload", w, "variant", fa.fa_variant_name(DT_CODE[w.dtype], w.d, w.causal, 1))
+    err = whole_parity(w)
+    say(err)
+    assert err["heads"] == w.B * w.H
+    assert_within(w, err, "whole tensor")
+
+
+# Sampled rows where the whole tensor would take the oracle minutes: every
+# boosted row, random rows, both rows around evenly spread query-block
+# boundaries of the default variant, and the first and last rows.
+SAMPLED = ["long_f16_causal_n65536_d64"]
+
+
+@pytest.mark.parametrize("name", SAMPLED)
+def test_full_size_sampled_rows(name):
+    w = WORKLOADS[name]
+    br = default_rows(w)
+    say("workload", w, "rows per block", br)
     err = sampled_parity(w, br)
     say(err)
     assert_within(w, err, "sampled")
+
+
+# ---- the positional entry point fa_fwd (null stream) ----
+
+@pytest.mark.parametrize("dt,d", [("f32", 64), ("f16", 128), ("bf16", 128), ("bf16", 256), ("f16", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fa_fwd_positional_entry_point(dt, d, causal):
+    """fa_fwd(Q,K,V,O,LSE,B,H,N_q,N_kv,d,scale,causal,dtype) on the null
+    stream: bitwise equal to fa_fwd_ex with the same arguments, and within
+    the dtype's tolerance of the oracle."""
+    w, x = random_problem(60 + d + int(causal), 2, 3, 301, 333, d, dt, causal)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    say("fa_fwd", dt, d, causal)
+    st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   w.B, w.H, w.n_q, w.n_kv, w.d, w.sm_scale, int(causal), DT_CODE[dt])
+    assert st == fa.FA_OK, fa.fa_strerror(st)
+    torch.cuda.synchronize()
+    o_ex, lse_ex = run_gpu(w, x)
+    assert torch.equal(o, o_ex) and torch.equal(lse, lse_ex)
+    from parity import errors, oracle_operands
+    import oracle
+    qo, ko, vo = oracle_operands(w, x)
+    o_ref, lse_ref = oracle.attention(qo, ko, vo, w.sm_scale, w.causal)
+    err = errors(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref)
+    say(err)
+    assert_within(w, err, "fa_fwd")
+    # LSE = NULL skips the statistic and leaves O unchanged
+    o2 = torch.empty_like(o)
+    st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), None,
+                   w.B, w.H, w.n_q, w.n_kv, w.d, w.sm_scale, int(causal), DT_CODE[dt])
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o)
+
+
+def test_fa_fwd_positional_e4m3_unit_descales():
+    """fa_fwd with FA_FP8_E4M3 uses descales of 1 (codes read as values)."""
+    w, x = random_problem(70, 1, 2, 200, 260, 128, "fp8_e4m3", False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    scale = 0.01
+    st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   w.B, w.H, w.n_q, w.n_kv, w.d, scale, 0, fa.FA_FP8_E4M3)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    o_ex, lse_ex = fa.fwd(q, k, v, scale=scale, descale=(1.0, 1.0, 1.0))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ex) and torch.equal(lse, lse_ex)
+
+
+def test_python_checks_reject_bad_outputs_before_launch():
+    """Mismatched out / lse / workspace tensors raise on the host."""
+    w, x = random_problem(71, 1, 2, 64, 64, 64, "bf16", False)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    with pytest.raises(ValueError):
+        fa.fwd(q, k, v, out=torch.empty(1, 2, 63, 64, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(TypeError):
+        fa.fwd(q, k, v, lse=torch.empty(1, 2, 64, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(TypeError):
+        fa.fwd(q, k.to(torch.float8_e4m3fn), v)
+    with pytest.raises(ValueError):
+        fa.fwd(q, k.transpose(2, 3).contiguous().transpose(2, 3), v)
+    with pytest.raises(TypeError):
+        fa.fwd_splitkv(q, k, v, workspace=torch.empty(1 << 20, dtype=torch.float32, device="cuda"))
+    o, lse = fa.fwd(q, k, v)
+    with pytest.raises(TypeError):
+        fa.bwd(q, k, v, o, lse.to(torch.bfloat16), o)
+    with pytest.raises(ValueError):
+        fa.bwd(q, k, v, o, lse, o[:, :, :32])
