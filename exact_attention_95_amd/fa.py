@@ -319,8 +319,8 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
     device tensor) is given.
     """
     import torch
-    check_tensors(q, k, v, out, lse, workspace=workspace, dtypes=(torch.bfloat16, torch.float16),
-                  out_dtype=q.dtype)
+    # an unsupported (but consistent) dtype is the C library's to report
+    check_tensors(q, k, v, out, lse, workspace=workspace, out_dtype=q.dtype)
     B, H, N_q, d = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
@@ -374,7 +374,7 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, s
     """
     import torch
     B, H, N_q, d = q.shape if q.dim() == 4 else (0, 0, 0, 0)
-    check_tensors(q, k, v, dtypes=(torch.bfloat16, torch.float16), workspace=workspace,
+    check_tensors(q, k, v, workspace=workspace,
                   extra=(("o", o, (B, H, N_q, d), q.dtype), ("do", do, (B, H, N_q, d), q.dtype),
                          ("lse", lse, (B, H, N_q), torch.float32)))
     B, H, N_q, d = q.shape
