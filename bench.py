@@ -83,12 +83,13 @@ KERNEL_SOURCE = {"f32": "fa_fwd32.hip", "f16": "fa_fwd16.hip", "bf16": "fa_fwd16
 
 
 def kernel_source_digest(dtype: str, bwd: bool = False) -> str:
-    """Hash of the sources that make the workload's kernel (its .hip file, the
-    shared device, tile and launch code), to tell whether stored counters
-    still apply."""
+    """Hash of the device sources that make the workload's kernels (its .hip
+    file and the shared device and tile headers), to tell whether stored
+    counters still apply.  Host code (validation, variant table) is left out:
+    the stored record names the variant it was taken on instead."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_95_amd", "csrc")
-    names = ["fa_device.h", "fa_internal.h", "fa_api.cpp", "fa_bwd16.hip" if bwd else KERNEL_SOURCE[dtype]]
+    names = ["fa_device.h", "fa_internal.h", "fa_bwd16.hip" if bwd else KERNEL_SOURCE[dtype]]
     if bwd or dtype in ("f16", "bf16"):
         names.append("fa_tile16.h")
     for name in sorted(names):
@@ -97,9 +98,9 @@ def kernel_source_digest(dtype: str, bwd: bool = False) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, dtype: str, bwd: bool = False):
+def stored_traffic(workload: str, dtype: str, variant: str, bwd: bool = False):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current kernel sources and the same variant; else None."""
     path = os.path.join(TRAFFIC_DIR, "traffic_%s%s.json" % (workload, "_bwd" if bwd else ""))
     if not os.path.exists(path):
         return None
@@ -107,7 +108,25 @@ def stored_traffic(workload: str, dtype: str, bwd: bool = False):
         rec = json.load(f)
     if rec.get("kernel_source_digest") != kernel_source_digest(dtype, bwd):
         return None
+    if rec.get("variant") != variant:
+        return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def variant_label(workload: str, tile: int = 0, splitkv=None, bwd: bool = False) -> str:
+    """The launch configuration a bench run of the workload times: the
+    backward, split-KV, or the forward tile variant's name (host-only)."""
+    from exact_attention_95_amd import fa
+    from exact_attention_95_amd.inputs import WORKLOADS
+    w = WORKLOADS[workload]
+    if bwd:
+        return "backward"
+    if splitkv is None and w.n_q <= 16:
+        splitkv = 0
+    if splitkv is not None and splitkv >= 0:
+        return "split_kv(%s)" % ("auto" if splitkv == 0 else splitkv)
+    code = {"f32": fa.FA_F32, "f16": fa.FA_F16, "bf16": fa.FA_BF16, "fp8_e4m3": fa.FA_FP8_E4M3}[w.dtype]
+    return fa.fa_variant_name(code, w.d, w.causal, tile or 1)
 
 
 def cpu_model() -> str:
@@ -262,7 +281,8 @@ def cpu_baseline_bwd(w, x, dout, target_s: float = 15.0) -> dict:
     }
 
 
-def summarize_counters(workload: str, fetch_csv: str, write_csv: str, bwd: bool = False) -> dict:
+def summarize_counters(workload: str, fetch_csv: str, write_csv: str, variant: str,
+                       bwd: bool = False) -> dict:
     """HBM bytes per launch of the attention kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same
     counter reads for a plain 1 GiB device copy (hipMemcpy's copy kernel) run
@@ -296,6 +316,7 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str, bwd: bool 
     rec = {
         "workload": workload + ("_bwd" if bwd else ""),
         "kernel_source_digest": kernel_source_digest(WORKLOADS[workload].dtype, bwd),
+        "variant": variant,
         "fetch_bytes_raw": fetch, "fetch_factor": ff,
         "write_bytes_raw": write, "write_factor": wf,
         "hbm_bytes_per_launch": round(fetch * ff + write * wf),
@@ -591,7 +612,9 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.summarize_counters:
-        rec = summarize_counters(args.workload, *args.summarize_counters, bwd=args.bwd)
+        rec = summarize_counters(args.workload, *args.summarize_counters,
+                                 variant=variant_label(args.workload, args.tile, args.splitkv, args.bwd),
+                                 bwd=args.bwd)
         path = os.path.join(TRAFFIC_DIR, "traffic_%s.json" % rec["workload"])
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
@@ -771,10 +794,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.n_q, "N_kv": w.n_kv,
                    "d": w.d, "causal": w.causal, "dtype": w.dtype,
                    "dropout_p": args.dropout,
-                   "variant": ("backward" if args.bwd else
-                               "split_kv(%s)" % ("auto" if splitkv == 0 else splitkv)
-                               if splitkv is not None else
-                               fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1)),
+                   "variant": variant_label(w.name, args.tile, args.splitkv, args.bwd),
                    "flops_per_step": flops, "algorithmic_bytes_per_step": nbytes},
         # HBM bytes the two traffic models of the pages give for this launch,
         # beside the measured traffic (fwd only)
@@ -784,7 +804,9 @@ def main(argv=None) -> int:
                 fa.fa_variant_name(fargs.dtype, w.d, w.causal, args.tile or 1)))},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": stored_traffic(w.name, w.dtype, args.bwd),
+                     "traffic": stored_traffic(w.name, w.dtype,
+                                               variant_label(w.name, args.tile, args.splitkv, args.bwd),
+                                               args.bwd),
                      "kernel_ms": round(kernel_ms, 4)},
     }
     if extras and hbm_bound:
