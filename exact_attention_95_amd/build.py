@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_fwd8.hip", "fa_bwd16.hip", "fa_probe.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd16.hip", "fa_fwd32.hip", "fa_fwd8.hip", "fa_bwd16.hip", "fa_probe.hip",
+           "fa_noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -168,6 +168,7 @@ extern "C" const char *fa_strerror(int status) {
         case FA_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
         case FA_ERR_DROPOUT: return "dropout_p outside [0, 1), or dropout not supported here (fp16/bf16, d <= 128, not split-KV)";
         case FA_ERR_LONG_KV: return "N_kv above the single-pass limit of 2^20 keys per row; use fa_fwd_splitkv";
+        case FA_ERR_SCRATCH: return "split-KV partials exceed the 64 MiB static scratch buffer of fa_fwd_splitkv_noalloc; use fa_fwd_splitkv with a workspace";
         default: return "unknown status";
     }
 }

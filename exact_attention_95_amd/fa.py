@@ -3,7 +3,7 @@
 The functions ``fa_fwd``, ``fa_fwd_ex``, ``fa_validate``, ``fa_strerror``,
 ``fa_num_variants``, ``fa_variant_name``, ``fa_fwd_splitkv``,
 ``fa_splitkv_workspace_bytes``, ``fa_bwd``, ``fa_bwd_validate``,
-``fa_bwd_workspace_bytes``, ``fa_dropout_mask`` and the measurement probes
+``fa_bwd_workspace_bytes``, ``fa_dropout_mask``, ``fa_fwd_splitkv_noalloc`` and the measurement probes
 ``fa_probe``, ``fa_probe_work_per_iter`` and ``fa_probe_wall_clock_khz``
 (include/fa_probe.h) mirror the C entry points of the same names.  ``fwd``
 is the torch convenience form: it allocates O and LSE with torch on the
@@ -22,12 +22,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_F32, FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2, 3
 (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_SCALE,
  FA_ERR_ALIAS, FA_ERR_DEVICE, FA_ERR_LAUNCH, FA_ERR_VARIANT, FA_ERR_WORKSPACE, FA_ERR_DROPOUT,
- FA_ERR_LONG_KV) = range(14)
-FA_MAX_NKV_SINGLE_PASS = 1 << 20  # include/fa.h
+ FA_ERR_LONG_KV, FA_ERR_SCRATCH) = range(15)
+FA_MAX_NKV_SINGLE_PASS = 1 << 20     # include/fa.h
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/fa.h
 
 EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variants",
             "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_bwd",
-            "fa_bwd_validate", "fa_bwd_workspace_bytes", "fa_dropout_mask")
+            "fa_bwd_validate", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd_splitkv_noalloc")
 # measurement probes (include/fa_probe.h)
 PROBE_EXPORTED = ("fa_probe", "fa_probe_work_per_iter", "fa_probe_wall_clock_khz")
 (FA_PROBE_MFMA_BF16, FA_PROBE_MFMA_F16, FA_PROBE_MFMA_FP8, FA_PROBE_MFMA_F32, FA_PROBE_EXP,
@@ -102,6 +103,8 @@ def load(path: str = LIB_PATH):
             lib.fa_variant_name.argtypes = [ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
             lib.fa_fwd_splitkv.restype = ctypes.c_int
             lib.fa_fwd_splitkv.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int, vp, i64]
+            lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+            lib.fa_fwd_splitkv_noalloc.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int]
             lib.fa_splitkv_workspace_bytes.restype = i64
             lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.POINTER(FaFwdArgs), ctypes.c_int]
             lib.fa_bwd.restype = ctypes.c_int
@@ -150,6 +153,10 @@ def fa_variant_name(dtype: int, d: int, causal: bool, v: int) -> str:
 
 def fa_fwd_splitkv(args: FaFwdArgs, num_splits: int, workspace, workspace_bytes: int) -> int:
     return load().fa_fwd_splitkv(ctypes.byref(args), num_splits, workspace, workspace_bytes)
+
+
+def fa_fwd_splitkv_noalloc(args: FaFwdArgs, num_splits: int) -> int:
+    return load().fa_fwd_splitkv_noalloc(ctypes.byref(args), num_splits)
 
 
 def fa_splitkv_workspace_bytes(args: FaFwdArgs, num_splits: int) -> int:
@@ -310,13 +317,14 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None,
 
 def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int = 0,
                 out=None, lse=None, with_lse: bool = True, stream=None, tile: int = 0,
-                workspace=None):
+                workspace=None, noalloc: bool = False):
     """Split-KV attention forward (bf16/fp16, d in {64, 128}); returns (O, LSE).
 
     Same contract as ``fwd``; the key range is processed in ``num_splits``
     chunks (0: library choice) whose partials are merged on the GPU.  The
     float32 workspace is allocated with torch unless ``workspace`` (a uint8
-    device tensor) is given.
+    device tensor) is given, or unless ``noalloc``: then the partials go to
+    the library's static scratch buffer (``fa_fwd_splitkv_noalloc``).
     """
     import torch
     # an unsupported (but consistent) dtype is the C library's to report
@@ -330,6 +338,14 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
         lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
     stream = _stream_handle(stream, q.device)
     args = make_args(q, k, v, out, lse, scale, causal, (1.0, 1.0, 1.0), stream, tile)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        with torch.cuda.device(q.device):
+            st = fa_fwd_splitkv_noalloc(args, num_splits)
+        if st != FA_OK:
+            raise FaError(st)
+        return out, lse
     need = fa_splitkv_workspace_bytes(args, num_splits)
     if need < 0:
         raise FaError(fa_validate(args) or FA_ERR_VARIANT)

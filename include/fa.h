@@ -82,7 +82,8 @@ typedef enum {
     FA_ERR_VARIANT = 10,  /* no compiled variant for this problem / tile_override out of range */
     FA_ERR_WORKSPACE = 11, /* split-KV or backward workspace NULL, misaligned or too small */
     FA_ERR_DROPOUT = 12,   /* dropout_p outside [0, 1), or dropout where it is not supported */
-    FA_ERR_LONG_KV = 13    /* N_kv above FA_MAX_NKV_SINGLE_PASS for fa_fwd / fa_fwd_ex */
+    FA_ERR_LONG_KV = 13,   /* N_kv above FA_MAX_NKV_SINGLE_PASS for fa_fwd / fa_fwd_ex */
+    FA_ERR_SCRATCH = 14    /* fa_fwd_splitkv_noalloc: partials exceed FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Longest key range per row the single-pass forward accepts (see "Very
@@ -183,6 +184,25 @@ int fa_validate(const fa_fwd_args *args);
  */
 int fa_fwd_splitkv(const fa_fwd_args *args, int num_splits, void *workspace,
                    int64_t workspace_bytes);
+
+/* Size of the static device buffer behind fa_fwd_splitkv_noalloc. */
+#define FA_NOALLOC_SCRATCH_BYTES (64 << 20)
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, result and kernels as
+ * fa_fwd_splitkv, but the float32 partials go to a static device buffer of
+ * FA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on every device
+ * it runs on until the process ends; the call allocates nothing.  The
+ * caller still passes Q, K, V, O and LSE.  FA_ERR_SCRATCH (before any HIP
+ * call) when fa_splitkv_workspace_bytes(args, num_splits) exceeds the
+ * buffer: decode shapes need far less (one query row, 256 heads, d = 128: 0.5
+ * MiB).  Every call on one device shares that device's buffer: calls on one
+ * stream are ordered, but calls that may overlap (other streams, other host
+ * threads) race on it and must be serialised by the caller.
+ */
+int fa_fwd_splitkv_noalloc(const fa_fwd_args *args, int num_splits);
 
 /*
  * Workspace bytes fa_fwd_splitkv needs for these arguments and num_splits

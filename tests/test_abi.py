@@ -149,7 +149,7 @@ def declared_statuses(header=HEADER):
 def test_strerror_names_every_status():
     statuses = declared_statuses()
     assert [v for _, v in statuses] == list(range(len(statuses)))  # dense, from 0
-    assert len(statuses) == 14
+    assert len(statuses) == 15
     for name, value in statuses:
         assert getattr(fa, name) == value, name  # the binding mirrors the header
     msgs = {fa.fa_strerror(v) for _, v in statuses}
@@ -406,3 +406,27 @@ def test_tensor_checks_run_before_any_launch():
     # every public entry point refuses CPU tensors before touching the library's kernels
     with pytest.raises(RuntimeError, match="GPU"):
         fa.fwd_splitkv(q, k, k)
+
+
+def test_noalloc_entry_point_host_checks():
+    """fa_fwd_splitkv_noalloc: argument errors and the scratch limit are
+    reported before any HIP call; empty problems are no-ops."""
+    text = open(HEADER).read()
+    assert re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(64 << 20\)", text)
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 64 << 20
+    lib = fa.load()
+    assert lib.fa_fwd_splitkv_noalloc(None, 0) == fa.FA_ERR_NULL
+    assert fa.fa_fwd_splitkv_noalloc(good_args(B=0), 0) == fa.FA_OK
+    assert fa.fa_fwd_splitkv_noalloc(good_args(d=96), 0) == fa.FA_ERR_HEAD_DIM
+    assert fa.fa_fwd_splitkv_noalloc(good_args(d=256), 0) == fa.FA_ERR_VARIANT
+    assert fa.fa_fwd_splitkv_noalloc(good_args(), -1) == fa.FA_ERR_SHAPE
+    assert fa.fa_fwd_splitkv_noalloc(good_args(dropout_p=0.2), 0) == fa.FA_ERR_DROPOUT
+    # 64 heads of 4096 rows at d = 128: one chunk, 128 MiB of partials
+    big = good_args(B=1, H=64, N_q=4096, N_kv=8192, d=128, Q=1 << 36, K=1 << 37, V=1 << 38,
+                    O=1 << 39, LSE=1 << 40)
+    assert fa.fa_splitkv_workspace_bytes(big, 0) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_fwd_splitkv_noalloc(big, 0) == fa.FA_ERR_SCRATCH
+    # the decode shape of the benchmark fits with room to spare
+    dec = good_args(B=8, H=32, N_q=1, N_kv=65536, d=128, Q=1 << 36, K=1 << 37, V=1 << 38,
+                    O=1 << 39, LSE=1 << 40)
+    assert 0 < fa.fa_splitkv_workspace_bytes(dec, 0) <= fa.FA_NOALLOC_SCRATCH_BYTES // 64
