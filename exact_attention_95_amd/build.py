@@ -28,6 +28,14 @@ COMMON = [
 ]
 
 
+# Per-file flags.  fa_fwd16.hip: MFMA results in arch VGPRs.  Only its d = 256
+# kernels are affected (the others use no AGPRs; their code is unchanged):
+# these keep the read-only Q operand in AGPRs, which the MFMAs read directly,
+# and O in arch VGPRs; with the compiler's default choice O itself lived in
+# AGPRs and was copied between register files at the loop's joins.
+EXTRA_FLAGS = {"fa_fwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -37,7 +45,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -69,6 +69,10 @@ struct Cfg {
     static constexpr int LDI = TILE / (1024 * NW);        // copy instructions per wave per tile
     static constexpr int NVO = DB < 4 ? DB : 4;           // distinct V read offsets per lane
     static constexpr float TAU = 8.0f;
+    // d = 256 runs one wave per SIMD and needs more than the 256 arch VGPRs:
+    // the read-only Q operand (64 registers) is kept in AGPRs, which the
+    // MFMAs read directly, and O, S and P stay in arch VGPRs
+    static constexpr bool Q_IN_AGPR = D_ >= 256;
     static_assert(TILE % (1024 * NW) == 0, "tile must split into whole wave copies");
     static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -296,6 +300,14 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
         raised = false;  // O is still zero
     }
 
+    auto pin = [&]() {
+        if constexpr (C::Q_IN_AGPR) {
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) asm volatile("" : "+a"(qf[ks]));
+        }
+    };
+    pin();
+
     // One pipelined iteration for tile t (t % 2 == PAR): S_{t+1} and the
     // softmax of tile t+1 (into pn), PV of tile t (from pc).
     auto iteration = [&](auto par, int t, v8 (&pc)[C::KB][2], v8 (&pn)[C::KB][2]) {
@@ -321,6 +333,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
         } else {
             pv_tile<C>(o, vbuf(PAR), voff, pc);
         }
+        pin();
     };
     for (int t = 0; t < ntile; t += 2) {
         iteration(std::integral_constant<int, 0>(), t, p0, p1);
