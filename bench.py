@@ -575,6 +575,98 @@ def memory_report(names) -> list:
     return out
 
 
+# Every other workload of the forward table, and the backward, timed after
+# the headline's timed region (forward unless noted)
+OTHER_WORKLOADS = [("single_head_f32_n256_d64", "fwd"), ("gpt2_medium_bf16_n1024_d64", "fwd"),
+                   ("long_f16_causal_n4096_d64", "fwd"), ("long_f16_causal_n16384_d64", "fwd"),
+                   ("long_f16_causal_n65536_d64", "fwd"), ("headline_bf16_n8192_d128", "fwd"),
+                   ("headline_bf16_causal_n8192_d128", "fwd"), ("large_head_bf16_n16384_d256", "fwd"),
+                   ("fp8_e4m3_n16384_d128", "fwd"), ("decode_bf16_b8_h32_nkv65536_d128", "splitkv"),
+                   ("headline_bf16_n8192_d128", "bwd")]
+
+
+def device_inputs(w, dev):
+    """Seeded N(0,1) inputs of w's shape drawn on the device (torch's generator;
+    fast for the large shapes), cast as make_inputs does: 16-bit by RNE, E4M3
+    with per-tensor absmax scaling to 448, and w.boost on a fraction of Q's
+    rows.  For timing only; parity runs on the oracle's inputs."""
+    import torch
+    from exact_attention_95_amd.inputs import DTYPES, E4M3_MAX
+    g = torch.Generator(device=dev).manual_seed(1000 + w.seed_id)
+    q = torch.randn((w.B, w.H, w.n_q, w.d), generator=g, device=dev)
+    k = torch.randn((w.B, w.H, w.n_kv, w.d), generator=g, device=dev)
+    v = torch.randn((w.B, w.H, w.n_kv, w.d), generator=g, device=dev)
+    if w.boost_frac:
+        rows = torch.randperm(w.B * w.H * w.n_q, generator=g, device=dev)[:int(w.boost_frac * w.B * w.H * w.n_q)]
+        q.view(-1, w.d)[rows] *= w.boost
+    if w.dtype == "fp8_e4m3":
+        out, desc = [], []
+        for t in (q, k, v):
+            sc = E4M3_MAX / float(t.abs().max())
+            out.append((t * sc).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn))
+            desc.append(1.0 / sc)
+        return out[0], out[1], out[2], tuple(desc)
+    dt = DTYPES[w.dtype]
+    return q.to(dt), k.to(dt), v.to(dt), (1.0, 1.0, 1.0)
+
+
+def other_workloads(dev, seconds: float = 0.6) -> list:
+    """Each workload of OTHER_WORKLOADS in its default launch configuration,
+    run back to back for about `seconds` on device-drawn inputs with the
+    shader clock and package power sampled: ms per call (HIP events),
+    TFLOP/s (decode: GB/s of algorithmic bytes), fraction of the dtype's
+    peak, and joules per TFLOP."""
+    import torch
+    from exact_attention_95_amd import fa
+    from exact_attention_95_amd.inputs import WORKLOADS
+    out = []
+    for name, kind in OTHER_WORKLOADS:
+        w = WORKLOADS[name]
+        q, k, v, desc = device_inputs(w, dev)
+        od = torch.bfloat16 if w.dtype == "fp8_e4m3" else q.dtype
+        o = torch.empty(q.shape, dtype=od, device=dev)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        stream = torch.cuda.Stream(device=dev)
+        args = fa.make_args(q, k, v, o, lse, w.sm_scale, w.causal, desc, stream.cuda_stream, 0)
+        keep = []
+        if kind == "splitkv":
+            ws = torch.empty(max(fa.fa_splitkv_workspace_bytes(args, 0), 256), dtype=torch.uint8, device=dev)
+            keep.append(ws)
+            fn = lambda: fa.fa_fwd_splitkv(args, 0, ws.data_ptr(), ws.numel())
+        elif kind == "bwd":
+            with torch.cuda.stream(stream):
+                fa.fa_fwd_ex(args)
+            do = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(4), device=dev).to(q.dtype)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            bargs = fa.make_bwd_args(q, k, v, o, lse, do, dq, dk, dv, w.sm_scale, w.causal, stream.cuda_stream)
+            ws = torch.empty(max(fa.fa_bwd_workspace_bytes(bargs), 256), dtype=torch.uint8, device=dev)
+            keep += [do, dq, dk, dv, ws]
+            fn = lambda: fa.fa_bwd(bargs, ws.data_ptr(), ws.numel())
+        else:
+            fn = lambda: fa.fa_fwd_ex(args)
+        st = fn()
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+        r = timed_with_clock(fn, stream, seconds)
+        flops = w.bwd_flops if kind == "bwd" else w.flops
+        rec = {"workload": name, "pass": kind, "variant": variant_label(name, bwd=(kind == "bwd")),
+               "ms": r["ms"], "calls": r["calls"], "sclk_mhz_median": r["sclk_mhz_median"],
+               "power_w_median": r["power_w_median"]}
+        if kind == "splitkv":
+            gbs = algorithmic_bytes(w) / (r["ms"] * 1e-3) / 1e9
+            rec.update(GBps=round(gbs, 1), frac=round(gbs / PEAK_HBM_GBS, 4), bound="hbm")
+        else:
+            tf = flops / (r["ms"] * 1e-3) / 1e12
+            rec.update(tflops=round(tf, 1), frac=round(tf / PEAK_TFLOPS[w.dtype], 4), bound="mfma")
+            if r["power_w_median"]:
+                rec["joules_per_tflop"] = round(r["power_w_median"] * r["ms"] * 1e-3 / (flops / 1e12), 4)
+        out.append(rec)
+        del q, k, v, o, lse, keep, args
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -606,6 +698,10 @@ def main(argv=None) -> int:
                     help="time the forward on the seeded inputs and on all-zero inputs, and "
                          "hipBLASLt's 8192^3 bf16 GEMM on N(0,1) and on zero operands, with the "
                          "shader clock sampled, print one JSON line and exit")
+    ap.add_argument("--other-workloads", type=int, default=1,
+                    help="1 (default): after the timed region, also time every other forward "
+                         "workload, the split-KV decode and the backward (about 1 s each) and add "
+                         "them to the JSON line; 0: skip")
     ap.add_argument("--memory-report", action="store_true",
                     help="print device memory of the long causal fp16 workloads vs a "
                          "materialised N x N baseline and exit")
@@ -754,10 +850,19 @@ def main(argv=None) -> int:
         # shader clock and package power while the same step runs back to back
         # for about a second (random data: the board's power cap sets the clock)
         under = timed_with_clock(step, stream, 1.0)
+        flops_step = w.bwd_flops if args.bwd else w.flops
         extras["device"]["under_kernel"] = {
             "ms": under["ms"], "sclk_mhz_median": under["sclk_mhz_median"],
             "power_w_median": under["power_w_median"],
-            "power_cap_w": read_watts(hwmon_power_files()[1])}
+            "power_cap_w": read_watts(hwmon_power_files()[1]),
+            # energy per unit of work under the cap: power x time / FLOPs
+            "joules_per_tflop": (round(under["power_w_median"] * under["ms"] * 1e-3 / (flops_step / 1e12), 4)
+                                 if under["power_w_median"] else None)}
+        if (args.other_workloads and w.name == DEFAULT_WORKLOAD and not args.bwd and splitkv is None
+                and args.dropout == 0.0 and args.tile == 0):
+            # the forward table's other workloads and the backward, timed after
+            # the headline's timed region on device-drawn inputs
+            extras["other_workloads"] = other_workloads(dev)
 
     if args.copy_calibration:
         # a plain device-to-device copy of exactly 1 GiB (hipMemcpy's copy kernel)
