@@ -582,7 +582,7 @@ OTHER_WORKLOADS = [("single_head_f32_n256_d64", "fwd"), ("gpt2_medium_bf16_n1024
                    ("long_f16_causal_n65536_d64", "fwd"), ("headline_bf16_n8192_d128", "fwd"),
                    ("headline_bf16_causal_n8192_d128", "fwd"), ("large_head_bf16_n16384_d256", "fwd"),
                    ("fp8_e4m3_n16384_d128", "fwd"), ("decode_bf16_b8_h32_nkv65536_d128", "splitkv"),
-                   ("headline_bf16_n8192_d128", "bwd")]
+                   ("headline_bf16_n8192_d128", "bwd"), ("large_head_bf16_n16384_d256", "bwd")]
 
 
 def device_inputs(w, dev):
@@ -768,8 +768,8 @@ def main(argv=None) -> int:
                 raise fa.FaError(s)
     check = o
     if args.bwd:
-        if w.dtype not in ("bf16", "f16") or w.d not in (64, 128):
-            print("the backward covers bf16/fp16 with d in {64, 128}", file=sys.stderr)
+        if w.dtype not in ("bf16", "f16") or w.d not in (64, 128, 256):
+            print("the backward covers bf16/fp16 with d in {64, 128, 256}", file=sys.stderr)
             return 2
         # the forward's O and LSE, then the timed step is one fa_bwd call
         fwd_step = step

@@ -383,7 +383,7 @@ const int kBwdKeyBlock = 128;  // keys per workgroup of the dK/dV kernel
 extern "C" int fa_bwd_validate(const fa_bwd_args *a) {
     if (!a) return FA_ERR_NULL;
     if (a->dtype != FA_BF16 && a->dtype != FA_F16) return FA_ERR_DTYPE;
-    if (a->d != 64 && a->d != 128) return FA_ERR_HEAD_DIM;
+    if (a->d != 64 && a->d != 128 && a->d != 256) return FA_ERR_HEAD_DIM;
     if (a->B < 0 || a->H < 0 || a->N_q < 0 || a->N_kv < 1) return FA_ERR_SHAPE;
     if (a->N_q > kMaxRows || a->N_kv > kMaxRows) return FA_ERR_SHAPE;
     if (a->B > 0 && a->H > INT32_MAX / a->B) return FA_ERR_SHAPE;
@@ -394,7 +394,10 @@ extern "C" int fa_bwd_validate(const fa_bwd_args *a) {
         return FA_ERR_SHAPE;
     if (!isfinite(a->scale) || !isfinite((float)((double)a->scale * 1.4426950408889634)))
         return FA_ERR_SCALE;
-    if (dropout_p8(a->dropout_p) < 0) return FA_ERR_DROPOUT;
+    const int p8 = dropout_p8(a->dropout_p);
+    if (p8 < 0) return FA_ERR_DROPOUT;
+    // dropout instances exist for d <= 128, as in the forward
+    if (p8 > 0 && a->d > 128) return FA_ERR_DROPOUT;
     if (!find_bwd(a->dtype, a->d, a->causal)) return FA_ERR_HEAD_DIM;
     if (bh == 0) return FA_OK;  // nothing to read or write
     if (!a->K || !a->V || !a->dK || !a->dV) return FA_ERR_NULL;

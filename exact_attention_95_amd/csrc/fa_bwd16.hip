@@ -12,7 +12,10 @@
 //
 // with dP_ij = dO_i . v_j.  dQ and dK/dV are computed by separate kernels so
 // that every output element has exactly one writer (no atomics; results are
-// bitwise repeatable); the price is computing S and dP twice.
+// bitwise repeatable); the price is computing S and dP twice.  At d = 256 the
+// dK and dV accumulators of a wave (128 registers each) do not fit together
+// beside this wave's K and V rows, so the dK/dV kernel runs as two passes,
+// one accumulating dV (S and P only) and one dK (S, dP and dS).
 //
 // Both kernels use the 32x32x16 MFMA layouts of the forward kernel (the
 // tile helpers of fa_tile16.h).  In the dQ kernel a wave owns 32 query rows,
@@ -32,12 +35,15 @@ namespace {
 
 constexpr int kBwdTile = 64;  // rows per streamed tile (keys for dQ, queries for dK/dV)
 
-// DROP: the dropout keep mask of the forward is replayed.
-template <typename T_, int D_, int NW_, bool CAUSAL_, bool DROP_ = false>
+// DROP: the dropout keep mask of the forward is replayed.  PART (dK/dV
+// kernel): 0 accumulates dK and dV, 1 dV only, 2 dK only.
+template <typename T_, int D_, int NW_, bool CAUSAL_, bool DROP_ = false, int PART_ = 0>
 struct CfgB {
     typedef T_ T;
     static constexpr int D = D_, NW = NW_, BC = kBwdTile, NT = NW * 64, BR = 32 * NW;
     static constexpr bool CAUSAL = CAUSAL_, DROP = DROP_;
+    static constexpr int PART = PART_;
+    static constexpr bool WANT_DV = PART_ != 2, WANT_DK = PART_ != 1;
     static constexpr int RB = D * 2, NC = RB / 16, RPB = RB >= 256 ? 1 : 256 / RB;
     static constexpr int KX = (NC < 16 ? NC : 16) - 1, VX = (NC / 4 < 4 ? NC / 4 : 4) - 1;
     static constexpr int TILE = BC * RB;
@@ -112,20 +118,43 @@ __device__ __forceinline__ void qk_rows2(f32x16 &s, f32x16 &dp, const char *ablk
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     asm volatile("" : "+v"(koff0));
-    v8 a[C::KS], b[C::KS];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-        const int o = (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3);
-        a[ks] = *(const v8 *)(ablk + o);
-        b[ks] = *(const v8 *)(gblk + o);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    auto off = [&](int ks) { return (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3); };
     s = (f32x16){};
     dp = (f32x16){};
+    if constexpr (C::D <= 128) {
+        v8 a[C::KS], b[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-        s = M::mma(a[ks], f[ks], s);
-        dp = M::mma(b[ks], g[ks], dp);
+        for (int ks = 0; ks < C::KS; ++ks) {
+            a[ks] = *(const v8 *)(ablk + off(ks));
+            b[ks] = *(const v8 *)(gblk + off(ks));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = M::mma(a[ks], f[ks], s);
+            dp = M::mma(b[ks], g[ks], dp);
+        }
+    } else {
+        // d = 256: all 32 operand reads up front would take 128 registers;
+        // a rolling window of L k-steps ahead instead, each step a
+        // scheduling region of its own
+        constexpr int L = 4;
+        v8 a[L], b[L];
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            a[j] = *(const v8 *)(ablk + off(j));
+            b[j] = *(const v8 *)(gblk + off(j));
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            s = M::mma(a[ks % L], f[ks], s);
+            dp = M::mma(b[ks % L], g[ks], dp);
+            if (ks + L < C::KS) {
+                a[ks % L] = *(const v8 *)(ablk + off(ks + L));
+                b[ks % L] = *(const v8 *)(gblk + off(ks + L));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
@@ -162,6 +191,46 @@ __device__ __forceinline__ void pv_rows2(f32x16 (&o1)[C::DB], const char *blk1,
             o1[db] = M::mma(a1[k2][db], p1[k2], o1[db]);
             o2[db] = M::mma(a2[k2][db], p2[k2], o2[db]);
         }
+}
+
+// One product of one 32-row block, s = A f, as qk_rows2 (reads first).
+template <class C>
+__device__ __forceinline__ void qk_rows1(f32x16 &s, const char *ablk, int koff0,
+                                         const typename Mma16<typename C::T>::v8 (&f)[C::KS]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+    asm volatile("" : "+v"(koff0));
+    v8 a[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) a[ks] = *(const v8 *)(ablk + (koff0 ^ (32 * (ks & 7))) + 256 * (ks >> 3));
+    __builtin_amdgcn_sched_barrier(0);
+    s = (f32x16){};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) s = M::mma(a[ks], f[ks], s);
+}
+
+// One product of one 32-row block of pv_tile, o^T += A^T p, as pv_rows2.
+template <class C>
+__device__ __forceinline__ void pv_rows1(f32x16 (&o)[C::DB], const char *blk,
+                                         const typename Mma16<typename C::T>::v8 (&pv)[2],
+                                         const int (&voff)[C::NVO]) {
+    typedef Mma16<typename C::T> M;
+    typedef typename M::v8 v8;
+    v8 a[2][C::DB];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const char *base = blk + 16 * k2 * C::RB + voff[db & 3] + 256 * (db >> 2);
+            const i16x4 lo = lds_read_tr16(base);
+            const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+            a[k2][db] = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) o[db] = M::mma(a[k2][db], pv[k2], o[db]);
 }
 
 // S = K-tile rows x qf and dP = V-tile rows x gf for both 32-key blocks, with
@@ -468,7 +537,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
 
     v8 kf[C::KS], vf[C::KS];
     load_rows<C>(p.k + (int64_t)bh * n_kv * C::RB, kj, n_kv, kf, h);
-    load_rows<C>(p.v + (int64_t)bh * n_kv * C::RB, kj, n_kv, vf, h);
+    if (C::WANT_DK) load_rows<C>(p.v + (int64_t)bh * n_kv * C::RB, kj, n_kv, vf, h);
     const float c = p.c;
     DropQuad dc{};
     if (C::DROP) dc = make_drop_quad(p.p8, (unsigned)kj >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
@@ -513,11 +582,11 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
                 // dropout: P o keep for dV (the 1/(1-p) goes into the dV store),
                 // dP of a dropped element 0 and of a kept one scaled
                 const bool kept = !C::DROP || ((keep >> e) & 1u);
-                xp[e] = (T)(kept ? pr : 0.f);
-                xs[e] = (T)(pr * ((C::DROP ? (kept ? dp[r] * p.drop_scale : 0.f) : dp[r]) - dl));
+                if (C::WANT_DV) xp[e] = (T)(kept ? pr : 0.f);
+                if (C::WANT_DK) xs[e] = (T)(pr * ((C::DROP ? (kept ? dp[r] * p.drop_scale : 0.f) : dp[r]) - dl));
             }
-            pb[k2] = xp;
-            ds[k2] = xs;
+            if (C::WANT_DV) pb[k2] = xp;
+            if (C::WANT_DK) ds[k2] = xs;
         }
     };
     // One tile, software-pipelined over its two 32-row blocks in four
@@ -528,12 +597,27 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         const float *st = (const float *)sb;
         f32x16 s[2], dp[2];
         v8 pb[2][2], ds[2][2];
-        constexpr int NQK = 2 * C::KS, NPV = 4 * C::DB;  // MFMAs of two products, per block
+        constexpr int NPROD = C::PART == 0 ? 2 : 1;
+        constexpr int NQK = (C::WANT_DK ? 2 : 1) * C::KS, NPV = 2 * NPROD * C::DB;  // MFMAs per block
+        auto qk = [&](int blk) {
+            if (C::WANT_DK)
+                qk_rows2<C>(s[blk], dp[blk], qt + 32 * blk * C::RB, gt + 32 * blk * C::RB, koff, kf, vf);
+            else
+                qk_rows1<C>(s[blk], qt + 32 * blk * C::RB, koff, kf);
+        };
+        auto pv = [&](int blk) {
+            if (C::PART == 0)
+                pv_rows2<C>(dv, gt + 32 * blk * C::RB, pb[blk], dk, qt + 32 * blk * C::RB, ds[blk], voff);
+            else if (C::WANT_DV)
+                pv_rows1<C>(dv, gt + 32 * blk * C::RB, pb[blk], voff);
+            else
+                pv_rows1<C>(dk, qt + 32 * blk * C::RB, ds[blk], voff);
+        };
         // segment A: S, dP of block 0
-        qk_rows2<C>(s[0], dp[0], qt, gt, koff, kf, vf);
+        qk(0);
         __builtin_amdgcn_sched_barrier(0);
         // segment B: S, dP of block 1 under the VALU of block 0
-        qk_rows2<C>(s[1], dp[1], qt + 32 * C::RB, gt + 32 * C::RB, koff, kf, vf);
+        qk(1);
         elementwise(mk, t, st, 0, s[0], dp[0], pb[0], ds[0]);
 #pragma unroll
         for (int i = 0; i < NQK; ++i) {
@@ -542,7 +626,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         }
         __builtin_amdgcn_sched_barrier(0);
         // segment C: dV, dK of block 0 under the VALU of block 1
-        pv_rows2<C>(dv, gt, pb[0], dk, qt, ds[0], voff);
+        pv(0);
         elementwise(mk, t, st, 1, s[1], dp[1], pb[1], ds[1]);
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
@@ -551,7 +635,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         }
         __builtin_amdgcn_sched_barrier(0);
         // segment D: dV, dK of block 1
-        pv_rows2<C>(dv, gt + 32 * C::RB, pb[1], dk, qt + 32 * C::RB, ds[1], voff);
+        pv(1);
     };
     auto sync_issue = [&](int t) {
         wait_vm();
@@ -571,7 +655,10 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     auto pin = [&]() {
         // keeps the accumulators in AGPRs across iterations
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+        for (int db = 0; db < C::DB; ++db) {
+            if (C::WANT_DK) asm volatile("" : "+a"(dk[db]));
+            if (C::WANT_DV) asm volatile("" : "+a"(dv[db]));
+        }
     };
     // tile t with its buffers chosen at run time
     auto tile_rt = [&](auto mk, int t) {
@@ -610,15 +697,17 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     for (; t < ntile; ++t) tile_rt(std::integral_constant<bool, true>(), t);
     if (kj < n_kv) {
         const int64_t row = (int64_t)bh * n_kv + kj;
-        store_rows<C>(p.dk + row * C::RB, dk, p.scale, h);
-        store_rows<C>(p.dv + row * C::RB, dv, C::DROP ? p.drop_scale : 1.f, h);
+        if (C::WANT_DK) store_rows<C>(p.dk + row * C::RB, dk, p.scale, h);
+        if (C::WANT_DV) store_rows<C>(p.dv + row * C::RB, dv, C::DROP ? p.drop_scale : 1.f, h);
     }
 }
 
 template <typename T, int D, int NWQ, int NWK, bool CAUSAL, bool DROP>
 int launch_bwd_t(const BwdParams &p, void *stream) {
     typedef CfgB<T, D, NWQ, CAUSAL, DROP> CQ;
-    typedef CfgB<T, D, NWK, CAUSAL, DROP> CK;
+    // d = 256: the dK/dV kernel as two passes (dV, then dK), see above
+    typedef CfgB<T, D, NWK, CAUSAL, DROP, (D >= 256 ? 1 : 0)> CK;
+    typedef CfgB<T, D, NWK, CAUSAL, DROP, 2> CK2;
     hipStream_t st = (hipStream_t)stream;
     const int64_t rows = (int64_t)p.n_bh * p.n_q;
     if (rows > 0) {
@@ -630,13 +719,20 @@ int launch_bwd_t(const BwdParams &p, void *stream) {
     }
     const int nk = (p.n_kv + CK::BR - 1) / CK::BR;
     hipLaunchKernelGGL(bwd_dkdv_kernel<CK>, dim3(p.n_bh * nk), dim3(CK::NT), 0, st, p);
+    if constexpr (D >= 256) hipLaunchKernelGGL(bwd_dkdv_kernel<CK2>, dim3(p.n_bh * nk), dim3(CK2::NT), 0, st, p);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 template <typename T, int D, int NWQ, int NWK, bool CAUSAL>
 int launch_bwd(const BwdParams &p, void *stream) {
-    return p.p8 != 0 ? launch_bwd_t<T, D, NWQ, NWK, CAUSAL, true>(p, stream)
-                     : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
+    if constexpr (D >= 256) {
+        // no dropout instances at d = 256 (the forward has none either;
+        // fa_bwd_validate refuses it)
+        return p.p8 != 0 ? 1 : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
+    } else {
+        return p.p8 != 0 ? launch_bwd_t<T, D, NWQ, NWK, CAUSAL, true>(p, stream)
+                         : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
+    }
 }
 
 // The dropout keep mask as bytes, one 4 x 4 block of one slice per thread
@@ -685,6 +781,8 @@ const BwdVariant *bwd_variants(int *count) {
         FA_B16(__bf16, FA_BF16, 128, 8, 4, 0),  FA_B16(__bf16, FA_BF16, 128, 8, 4, 1),
         FA_B16(_Float16, FA_F16, 64, 8, 4, 0),  FA_B16(_Float16, FA_F16, 64, 8, 4, 1),
         FA_B16(_Float16, FA_F16, 128, 8, 4, 0), FA_B16(_Float16, FA_F16, 128, 8, 4, 1),
+        FA_B16(__bf16, FA_BF16, 256, 4, 4, 0),  FA_B16(__bf16, FA_BF16, 256, 4, 4, 1),
+        FA_B16(_Float16, FA_F16, 256, 4, 4, 0), FA_B16(_Float16, FA_F16, 256, 4, 4, 1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

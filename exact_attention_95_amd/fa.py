@@ -382,8 +382,8 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, s
         workspace=None, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
     """Attention backward of torch device tensors; returns (dQ, dK, dV).
 
-    q, o, do: [B,H,N_q,d]; k, v: [B,H,N_kv,d] (bf16 or fp16, contiguous, one
-    gfx950 device); lse: [B,H,N_q] float32.  o and lse must be the forward's
+    q, o, do: [B,H,N_q,d]; k, v: [B,H,N_kv,d] (bf16 or fp16, d in {64, 128,
+    256}, contiguous, one gfx950 device); lse: [B,H,N_q] float32.  o and lse must be the forward's
     outputs for these inputs, scale and causal.  The float32 workspace (D per
     query row) is allocated with torch unless ``workspace`` (a uint8 device
     tensor) is given.

@@ -230,7 +230,8 @@ int64_t fa_splitkv_workspace_bytes(const fa_fwd_args *args, int num_splits);
  * type.  dQ, dK, dV: device outputs with the type and layout of Q, K and V,
  * written in full; they must not overlap each other, the inputs or the
  * workspace (FA_ERR_ALIAS).  dtype: FA_BF16 or FA_F16 (else FA_ERR_DTYPE); d
- * in {64, 128} (else FA_ERR_HEAD_DIM).  Other rules as for fa_fwd_ex (shapes,
+ * in {64, 128, 256} (else FA_ERR_HEAD_DIM); dropout with d <= 128 only (as
+ * in the forward; FA_ERR_DROPOUT otherwise).  Other rules as for fa_fwd_ex (shapes,
  * 16-byte alignment, finite scale, top-left causal mask).  B or H equal to 0
  * is a no-op; N_q = 0 writes dK = dV = 0.
  */
@@ -274,7 +275,8 @@ int64_t fa_bwd_workspace_bytes(const fa_bwd_args *args);
  * otherwise); its contents are overwritten.  Three kernels run on
  * args->stream, in order: D from dO and O (and LSE log2(e) from LSE), then dQ
  * (one workgroup per query block), then dK and dV (one workgroup per key
- * block).  No atomics: every
+ * block; at d = 256 as two kernels, dV then dK, each recomputing the scores,
+ * because both accumulators do not fit one wave's registers).  No atomics: every
  * output element is written by exactly one lane, so results are bitwise
  * repeatable.
  */

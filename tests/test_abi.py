@@ -283,7 +283,9 @@ def test_bwd_validate_accepts_good_args():
     (dict(dtype=fa.FA_F32), fa.FA_ERR_DTYPE),
     (dict(dtype=fa.FA_FP8_E4M3), fa.FA_ERR_DTYPE),
     (dict(dtype=9), fa.FA_ERR_DTYPE),
-    (dict(d=256), fa.FA_ERR_HEAD_DIM),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM),
+    (dict(d=512), fa.FA_ERR_HEAD_DIM),
+    (dict(d=256, dropout_p=0.1), fa.FA_ERR_DROPOUT),
     (dict(d=96), fa.FA_ERR_HEAD_DIM),
     (dict(N_kv=0), fa.FA_ERR_SHAPE),
     (dict(B=-1), fa.FA_ERR_SHAPE),
@@ -322,7 +324,8 @@ def test_bwd_validate_null_args_and_empty_problems():
 def test_bwd_workspace_bytes():
     a = good_bwd_args()
     assert fa.fa_bwd_workspace_bytes(a) == 2 * (-(-2 * 3 * 100 * 4 // 256) * 256)  # D, LSE log2(e)
-    assert fa.fa_bwd_workspace_bytes(good_bwd_args(d=256)) == -1
+    assert fa.fa_bwd_workspace_bytes(good_bwd_args(d=256)) == 2 * (-(-2 * 3 * 100 * 4 // 256) * 256)
+    assert fa.fa_bwd_workspace_bytes(good_bwd_args(d=96)) == -1
 
 
 def test_bwd_refuses_cpu_tensors():
@@ -353,6 +356,9 @@ def test_dropout_support_limits():
     assert fa.fa_splitkv_workspace_bytes(a, 0) == -1
     assert fa.fa_fwd_splitkv(a, 0, None, 0) == fa.FA_ERR_DROPOUT
     assert fa.fa_bwd_validate(good_bwd_args(dropout_p=0.3, dropout_seed=2**64 - 1, dropout_offset=7)) == fa.FA_OK
+    # d = 256: the backward runs without dropout only, as the forward
+    assert fa.fa_bwd_validate(good_bwd_args(d=256)) == fa.FA_OK
+    assert fa.fa_bwd_validate(good_bwd_args(d=256, dropout_p=0.2)) == fa.FA_ERR_DROPOUT
 
 
 def test_dropout_mask_entry_validation():

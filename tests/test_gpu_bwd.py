@@ -29,6 +29,12 @@ CASES = [
     (1, 1, 40, 1, 64, "bf16", False),
     (1, 1, 300, 37, 128, "f16", True),
     (1, 1, 1000, 1000, 128, "bf16", False),
+    # d = 256: dQ kernel with 4 waves, dK/dV as two passes (dV, then dK)
+    (1, 2, 200, 300, 256, "bf16", False),
+    (1, 2, 333, 333, 256, "bf16", True),
+    (2, 1, 130, 77, 256, "f16", True),
+    (1, 1, 64, 512, 256, "f16", False),
+    (1, 1, 1, 40, 256, "bf16", False),
 ]
 
 
@@ -73,8 +79,9 @@ def test_bwd_scales(scale):
         assert_grads_within(errs, "scale %g" % scale)
 
 
-def test_bwd_repeatable_and_key_gradients_sum_to_zero():
-    w, x = random_problem(421, 1, 2, 256, 320, 128, "bf16", False)
+@pytest.mark.parametrize("d", [128, 256])
+def test_bwd_repeatable_and_key_gradients_sum_to_zero(d):
+    w, x = random_problem(421, 1, 2, 256, 320, d, "bf16", False)
     dout = make_dout(w)
     a = run_bwd(w, x, dout)
     b = run_bwd(w, x, dout)
@@ -118,7 +125,7 @@ def test_bwd_errors():
 
 
 @pytest.mark.parametrize("name", ["headline_bf16_n8192_d128", "headline_bf16_causal_n8192_d128",
-                                  "gpt2_medium_bf16_n1024_d64"])
+                                  "gpt2_medium_bf16_n1024_d64", "large_head_bf16_n16384_d256"])
 def test_bwd_full_size_sampled(name):
     """Full-size backward in the launch configuration the benchmark times;
     the oracle checks dQ on sampled rows and dK, dV on sampled keys of two
