@@ -138,7 +138,9 @@ __device__ __forceinline__ void mask8(f32x16 (&s)[C::KB], int t0, int qi, int n_
 // 2^TAU; the kernel computes P' = 2^PSHIFT P = exp2(S c - m + PSHIFT)
 // directly, sums the float32 P' into l_acc and rounds P' to E4M3 into the P^T
 // operand; `raised` and alpha tell the caller to rescale O before
-// accumulating this tile.  softmax8_head takes the row max, the decision and
+// accumulating this tile.  Each pair of codes is written over the operand
+// word's previous contents, whose last reader was the P V product of the
+// tile before, so the half-word conversions need no zeroed register.  softmax8_head takes the row max, the decision and
 // block 0 of P' (words 0-3 of the operand); softmax8_tail block 1 (words 4-7)
 // with the same bias.  The loop runs the head under the PV MFMAs of the
 // previous tile and the tail under the S MFMAs of the next, so both halves of
@@ -169,7 +171,7 @@ __device__ __forceinline__ void softmax8_head(f32x16 (&s)[C::KB], i32x8 &pb, flo
             v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][4 * w4 + e], c, bias));
             l4[e] += v[e];
         }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], pb[w4], false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
         pb[w4] = word;
     }
@@ -186,7 +188,7 @@ __device__ __forceinline__ void softmax8_tail(const f32x16 &s1, i32x8 &pb, float
             v[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[4 * w4 + e], c, bias));
             l4[e] += v[e];
         }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], pb[4 + w4], false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
         pb[4 + w4] = word;
     }
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
     float m_use = kNegInf, l_acc = 0.f, alpha = 1.f;
     bool raised = false;
     const float c = p.c;
-    i32x8 p0, p1;
+    i32x8 p0 = (i32x8){}, p1 = (i32x8){};
 
     wait_vm();
     __syncthreads();
