@@ -57,23 +57,35 @@ struct CfgB {
     static_assert(TILE % (1024 * NW) == 0, "tile must split into whole wave copies");
 };
 
-// Per-lane LDS offsets of the two operand reads of a tile in the V-style
-// layout (vswz): row reads (k-step 0 of qk_tile; k-step ks is koff ^ 32 ks)
-// and transposed reads (pv_tile).
+// Per-lane LDS offsets of the two operand reads of a tile in the layout read
+// both ways (bswz): row reads (k-step 0 of qk_tile; k-step ks is koff ^ 32
+// ks) and transposed reads (pv_tile).
 template <class C>
-__device__ __forceinline__ int row_offset_v(int lane) {
+__device__ __forceinline__ int row_offset_b(int lane) {
     const int l32 = lane & 31, h = lane >> 5;
-    return l32 * C::RB + 16 * (h ^ vswz<C>(l32));
+    return l32 * C::RB + 16 * (h ^ bswz<C>(l32));
 }
+// A transposed operand is two reads, rows rsub and rsub + 8 of a 16-row
+// slice (slices start at multiples of 16 rows).  Row rsub + 8 has the
+// swizzle of row rsub with bit 1 flipped, so its offset is the first one
+// XOR 32, plus 8 rows.
+struct TrOffsets {
+    int lo[4], hi[4];
+};
 template <class C>
-__device__ __forceinline__ void tr_offsets(int lane, int (&voff)[C::NVO]) {
+__device__ __forceinline__ TrOffsets tr_offsets(int lane) {
     const int h = lane >> 5;
     const int j = lane & 15;
     const int rsub = 4 * h + (j >> 2);
-    const int x = vswz<C>(j >> 2) >> 2;
+    const int g = bswz<C>(rsub);
     const int y = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+    TrOffsets t;
 #pragma unroll
-    for (int db = 0; db < C::NVO; ++db) voff[db] = rsub * C::RB + 16 * (4 * (db ^ x) + y) + 8 * (j & 1);
+    for (int db = 0; db < 4; ++db) {
+        t.lo[db] = rsub * C::RB + 16 * (4 * (db ^ (g >> 2)) + (y ^ (g & 3))) + 8 * (j & 1);
+        t.hi[db] = (t.lo[db] ^ 32) + 8 * C::RB;
+    }
+    return t;
 }
 
 // This lane's row of a [n, d] slice as the 32x32x16 B operand (row r of the
@@ -166,22 +178,22 @@ template <class C>
 __device__ __forceinline__ void pv_rows2(f32x16 (&o1)[C::DB], const char *blk1,
                                          const typename Mma16<typename C::T>::v8 (&p1)[2], f32x16 (&o2)[C::DB],
                                          const char *blk2, const typename Mma16<typename C::T>::v8 (&p2)[2],
-                                         const int (&voff)[C::NVO]) {
+                                         const TrOffsets &vo) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     v8 a1[2][C::DB], a2[2][C::DB];
-    auto rd = [&](const char *base) {
-        const i16x4 lo = lds_read_tr16(base);
-        const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+    auto rd = [&](const char *blk, int k2, int db) {
+        const int base = 16 * k2 * C::RB + 256 * (db >> 2);
+        const i16x4 lo = lds_read_tr16(blk + base + vo.lo[db & 3]);
+        const i16x4 hi = lds_read_tr16(blk + base + vo.hi[db & 3]);
         return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const int off = 16 * k2 * C::RB + voff[db & 3] + 256 * (db >> 2);
-            a1[k2][db] = rd(blk1 + off);
-            a2[k2][db] = rd(blk2 + off);
+            a1[k2][db] = rd(blk1, k2, db);
+            a2[k2][db] = rd(blk2, k2, db);
         }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -213,7 +225,7 @@ __device__ __forceinline__ void qk_rows1(f32x16 &s, const char *ablk, int koff0,
 template <class C>
 __device__ __forceinline__ void pv_rows1(f32x16 (&o)[C::DB], const char *blk,
                                          const typename Mma16<typename C::T>::v8 (&pv)[2],
-                                         const int (&voff)[C::NVO]) {
+                                         const TrOffsets &vo) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     v8 a[2][C::DB];
@@ -221,9 +233,9 @@ __device__ __forceinline__ void pv_rows1(f32x16 (&o)[C::DB], const char *blk,
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const char *base = blk + 16 * k2 * C::RB + voff[db & 3] + 256 * (db >> 2);
-            const i16x4 lo = lds_read_tr16(base);
-            const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+            const char *base = blk + 16 * k2 * C::RB + 256 * (db >> 2);
+            const i16x4 lo = lds_read_tr16(base + vo.lo[db & 3]);
+            const i16x4 hi = lds_read_tr16(base + vo.hi[db & 3]);
             a[k2][db] = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     __builtin_amdgcn_sched_barrier(0);
@@ -275,16 +287,16 @@ __device__ __forceinline__ void qk_dq_rolling(f32x16 (&s)[C::KB], f32x16 (&dp)[C
 // o^T += V_tile^T P^T as pv_tile, with a rolling window of L MFMAs' operand
 // reads (two transposed reads each) ahead.
 template <class C, int L>
-__device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs, const int (&voff)[C::NVO],
+__device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs, const TrOffsets &vo,
                                               const typename Mma16<typename C::T>::v8 (&pb)[C::KB][2]) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
     constexpr int N = C::KB * 2 * C::DB;
     auto rd = [&](int i) {
         const int kb = i / (2 * C::DB), k2 = (i / C::DB) & 1, db = i % C::DB;
-        const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + voff[db & 3] + 256 * (db >> 2);
-        const i16x4 lo = lds_read_tr16(base);
-        const i16x4 hi = lds_read_tr16(base + 8 * C::RB);
+        const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + 256 * (db >> 2);
+        const i16x4 lo = lds_read_tr16(base + vo.lo[db & 3]);
+        const i16x4 hi = lds_read_tr16(base + vo.hi[db & 3]);
         return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     v8 buf[L];
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (batch*head, block of 32*NW query rows), streaming
-// K and V tiles of 64 keys.  K is stored in the V-style layout (read both by
+// K and V tiles of 64 keys.  K is stored in the layout read both ways (by
 // rows and transposed), V in the K-style layout (read by rows only).
 template <class C>
 __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p) {
@@ -367,8 +379,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     int wn = 0;
     if (wq0 < n_q) wn = !C::CAUSAL ? ntile : min(ntile, min(wq0 + 31, n_q - 1) / C::BC + 1);
 
-    const CopyPlan<C, true> kplan(w, lane);   // V-style layout
-    const CopyPlan<C, false> vplan(w, lane);  // K-style layout
+    const CopyPlan<C, kLayoutBoth> kplan(w, lane);
+    const CopyPlan<C, kLayoutK> vplan(w, lane);
     if (ntile > 0) {
         kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
         vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);
@@ -384,10 +396,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     DropQuad dr{};
     if (C::DROP) dr = make_drop_quad(p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
 
-    const int koff_k = row_offset_v<C>(lane);
+    const int koff_k = row_offset_b<C>(lane);
     const int koff_v = l32 * C::RB + 16 * (h ^ kswz<C>(l32));
-    int voff[C::NVO];
-    tr_offsets<C>(lane, voff);
+    const TrOffsets voff = tr_offsets<C>(lane);
 
     f32x16 dq[C::DB];
 #pragma unroll
@@ -471,7 +482,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (batch*head, block of 32*NW keys), streaming Q
-// and dO tiles of 64 query rows (both in the V-style layout: read by rows
+// and dO tiles of 64 query rows (both in the layout read both ways: by rows
 // and transposed) with the tiles' LSE_i log2(e) and D_i (LDS, after the
 // four tile buffers: [0, 256) LSE, [256, 512) D per buffer).
 template <class C>
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     const int t0 = C::CAUSAL ? min(k0 / C::BC, ntile) : 0;
     const int wt0 = C::CAUSAL ? min(wk0 / C::BC, ntile) : 0;  // this wave's first tile
 
-    const CopyPlan<C, true> plan(w, lane);
+    const CopyPlan<C, kLayoutBoth> plan(w, lane);
     // LSE and D of tile t (wave 0: lanes 0-15 fetch LSE rows 4i..4i+3, lanes
     // 16-31 the same rows of D); rows past n_q read as 0 through the buffer
     // descriptors' bounds (their P is forced to 0 below)
@@ -541,9 +552,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     const float c = p.c;
     DropQuad dc{};
     if (C::DROP) dc = make_drop_quad(p.p8, (unsigned)kj >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
-    const int koff = row_offset_v<C>(lane);
-    int voff[C::NVO];
-    tr_offsets<C>(lane, voff);
+    const int koff = row_offset_b<C>(lane);
+    const TrOffsets voff = tr_offsets<C>(lane);
 
     f32x16 dk[C::DB], dv[C::DB];
 #pragma unroll

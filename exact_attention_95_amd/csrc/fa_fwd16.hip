@@ -241,8 +241,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
         return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > rwq0);
     };
 
-    const CopyPlan<C, false> kplan(w, lane);
-    const CopyPlan<C, true> vplan(w, lane);
+    const CopyPlan<C, kLayoutK> kplan(w, lane);
+    const CopyPlan<C, kLayoutV> vplan(w, lane);
     if (ntile > 0) {
         kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
         vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);

@@ -36,12 +36,22 @@ template <class C> __device__ __forceinline__ int kswz(int r) { return (r / C::R
 // reads cover 4 consecutive rows x 4 chunks per half-wave, which this XOR
 // spreads over 16 different bank groups.
 template <class C> __device__ __forceinline__ int vswz(int r) { return 4 * ((r / C::RPB) & C::VX); }
+// Rows read both ways (by rows and transposed): chunk c of row r is stored at
+// chunk c ^ bswz(r).  The bits of vswz keep the four rows of a half-wave's
+// transposed read in four different 64-byte bank ranges; the two low bits,
+// taken from bits 2-3 of the row, make the 16 rows of a row read land on 16
+// different bank groups (with vswz alone they share four).
+template <class C> __device__ __forceinline__ int bswz(int r) { return vswz<C>(r) | ((r >> 2) & 3); }
 
-// Per-lane part of the direct-to-LDS copies of one K (or V) tile: copy
-// instruction i of wave w moves chunks cb..cb+63 (cb = (i*NW + w)*64) of the
-// tile's LDS image; this lane's chunk is row r, physical chunk pc, so it
-// fetches logical chunk pc ^ swizzle(r) of row r.
-template <class C, bool IS_V>
+// Tile layouts: K-style (row reads only), V-style (transposed reads only),
+// or both.
+enum { kLayoutK = 0, kLayoutV = 1, kLayoutBoth = 2 };
+
+// Per-lane part of the direct-to-LDS copies of one tile in layout LAYOUT:
+// copy instruction i of wave w moves chunks cb..cb+63 (cb = (i*NW + w)*64)
+// of the tile's LDS image; this lane's chunk is row r, physical chunk pc, so
+// it fetches logical chunk pc ^ swizzle(r) of row r.
+template <class C, int LAYOUT>
 struct CopyPlan {
     // Offsets are kept in registers only when there are few of them; wide
     // heads (many copies per wave, many live accumulators) recompute them.
@@ -51,7 +61,7 @@ struct CopyPlan {
         const int chunk = (i * C::NW + w) * 64 + lane;
         const int r = chunk / C::NC;
         const int pc = chunk % C::NC;
-        const int sw = IS_V ? vswz<C>(r) : kswz<C>(r);
+        const int sw = LAYOUT == kLayoutBoth ? bswz<C>(r) : LAYOUT == kLayoutV ? vswz<C>(r) : kswz<C>(r);
         *row = r;
         return (unsigned)(r * C::RB + 16 * (pc ^ sw));
     }
