@@ -26,6 +26,8 @@
 // this wave's K and V rows in registers), and dV^T += dO^T P, dK^T += Q^T dS
 // read dO and Q transposed.  LSE_i and D_i vary along the accumulator's rows
 // there, so they are staged through LDS with the tiles.
+#include <utility>
+
 #include "fa_device.h"
 #include "fa_tile16.h"
 #include "../../include/fa.h"
@@ -34,6 +36,17 @@ namespace fa {
 namespace {
 
 constexpr int kBwdTile = 64;  // rows per streamed tile (keys for dQ, queries for dK/dV)
+
+// f(integral_constant<int, I>) for I = 0 .. N-1 in order, each with a
+// compile-time index (a long #pragma unroll loop is not always unrolled)
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 // DROP: the dropout keep mask of the forward is replayed.  PART (dK/dV
 // kernel): 0 accumulates dK and dV, 1 dV only, 2 dK only.
@@ -647,6 +660,103 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         // segment D: dV, dK of block 1
         pv(1);
     };
+    // The same tile (both products, no dropout, d = 128) as one stream of
+    // MFMAs with every operand read issued RL steps ahead of its MFMA, across
+    // the segment boundaries, so that no segment starts by waiting for its
+    // reads.  Steps [0, NQ): S and dP of block 0; [NQ, 2 NQ): those of block
+    // 1; [2 NQ, 2 NQ + NP): dV and dK of block 0; then those of block 1.  The
+    // VALU of block 0 runs one element (d = 64: two) per step over steps
+    // NQ + 1 .. 2 NQ, after the last dP MFMA of block 0 has had a step to
+    // finish; that of block 1 over steps 2 NQ + 1 .. 3 NQ.  Each block's
+    // first 8 elements (k2 = 0) are complete before its first dV/dK MFMA,
+    // the other 8 before the first MFMA that reads them (k2 = 1).
+    auto body_roll = [&](auto mk, int t, const char *qt, const char *gt, const char *sb) {
+        constexpr bool MK = decltype(mk)::value;
+        constexpr int NQ = 2 * C::KS, NP = 4 * C::DB, N = 2 * (NQ + NP), RL = 4;
+        constexpr int EPS = 16 / NQ;  // elements per step
+        static_assert(NQ == NP && 16 % NQ == 0, "one VALU window per product segment");
+        const float *st = (const float *)sb;
+        f32x16 s[2], dp[2];
+        v8 pb[2][2], ds[2][2];
+        f32x4 stt[2][4];  // LSE and D of the block whose VALU runs: [k2][l_lo, l_hi, d_lo, d_hi]
+        auto rd = [&](int i) -> v8 {
+            if (i < 2 * NQ) {
+                const int blk = i / NQ, j = i % NQ, ks = j >> 1;
+                const char *base = ((j & 1) ? gt : qt) + 32 * blk * C::RB;
+                return *(const v8 *)(base + ((koff ^ (32 * (ks & 7))) + 256 * (ks >> 3)));
+            }
+            const int i2 = i - 2 * NQ, blk = i2 / NP, j = i2 % NP;
+            const int k2 = j / (2 * C::DB), db = (j >> 1) % C::DB;
+            const char *base = ((j & 1) ? qt : gt) + (32 * blk + 16 * k2) * C::RB + 256 * (db >> 2);
+            const i16x4 lo = lds_read_tr16(base + voff.lo[db & 3]);
+            const i16x4 hi = lds_read_tr16(base + voff.hi[db & 3]);
+            return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        auto load_stats = [&](int kb) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                stt[k2][0] = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 4 * h);
+                stt[k2][1] = *(const f32x4 *)(st + 32 * kb + 16 * k2 + 8 + 4 * h);
+                stt[k2][2] = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 4 * h);
+                stt[k2][3] = *(const f32x4 *)(st + 64 + 32 * kb + 16 * k2 + 8 + 4 * h);
+            }
+        };
+        // element x (k2 = x / 8, e = x % 8) of P and dS of block kb
+        auto elem = [&](int kb, int x) {
+            const int k2 = x >> 3, e = x & 7, r = 8 * k2 + e;
+            const float l2 = e < 4 ? stt[k2][0][e & 3] : stt[k2][1][e & 3];
+            const float dl = e < 4 ? stt[k2][2][e & 3] : stt[k2][3][e & 3];
+            float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -l2));
+            if (MK) {
+                const int q = t * C::BC + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                pr = (q < n_q && (!C::CAUSAL || kj <= q)) ? pr : 0.f;
+            }
+            pb[kb][k2][e] = (T)pr;
+            ds[kb][k2][e] = (T)(pr * (dp[kb][r] - dl));
+        };
+        v8 buf[RL];
+#pragma unroll
+        for (int j = 0; j < RL; ++j) buf[j] = rd(j);
+        static_for<N>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const v8 a = buf[i % RL];
+            if (i < 2 * NQ) {
+                const int blk = i / NQ, j = i % NQ, ks = j >> 1;
+                if (j & 1)
+                    dp[blk] = M::mma(a, vf[ks], ks == 0 ? (f32x16){} : dp[blk]);
+                else
+                    s[blk] = M::mma(a, kf[ks], ks == 0 ? (f32x16){} : s[blk]);
+            } else {
+                const int i2 = i - 2 * NQ, blk = i2 / NP, j = i2 % NP;
+                const int k2 = j / (2 * C::DB), db = (j >> 1) % C::DB;
+                if (j & 1)
+                    dk[db] = M::mma(a, ds[blk][k2], dk[db]);
+                else
+                    dv[db] = M::mma(a, pb[blk][k2], dv[db]);
+            }
+            if (i + RL < N) buf[i % RL] = rd(i + RL);
+            if (i == NQ) load_stats(0);
+            if (i > NQ && i <= 2 * NQ) {
+#pragma unroll
+                for (int u = 0; u < EPS; ++u) elem(0, (i - NQ - 1) * EPS + u);
+            }
+            // after block 0's last element, which runs in this same step
+            if (i == 2 * NQ) load_stats(1);
+            if (i > 2 * NQ && i <= 3 * NQ) {
+#pragma unroll
+                for (int u = 0; u < EPS; ++u) elem(1, (i - 2 * NQ - 1) * EPS + u);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // (at d = 64 the two waves per SIMD leave no room for the read window)
+    constexpr bool ROLL = !C::DROP && C::PART == 0 && C::D == 128;
+    auto run_body = [&](auto mk, int t, const char *qt, const char *gt, const char *sb) {
+        if constexpr (ROLL)
+            body_roll(mk, t, qt, gt, sb);
+        else
+            body(mk, t, qt, gt, sb);
+    };
     auto sync_issue = [&](int t) {
         wait_vm();
         __syncthreads();
@@ -674,7 +784,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
     auto tile_rt = [&](auto mk, int t) {
         sync_issue(t);
         const int b = t & 1;
-        body(mk, t, qbuf(b), gbuf(b), sbuf(b));
+        run_body(mk, t, qbuf(b), gbuf(b), sbuf(b));
         pin();
     };
     // tile t of parity PAR, buffers fixed
@@ -687,7 +797,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
             plan.issue(gh, (t + 1) * C::BC, n_q, PAR ? sg0 : sg1, w, lane);
             issue_stats(t + 1, PAR ? ss0 : ss1);
         }
-        body(std::integral_constant<bool, false>(), t, PAR ? sq1 : sq0, PAR ? sg1 : sg0, PAR ? ss1 : ss0);
+        run_body(std::integral_constant<bool, false>(), t, PAR ? sq1 : sq0, PAR ? sg1 : sg0, PAR ? ss1 : ss0);
         pin();
     };
     int t = t0;
