@@ -81,10 +81,16 @@ __device__ __forceinline__ int row_offset_b(int lane) {
 // A transposed operand is two reads, rows rsub and rsub + 8 of a 16-row
 // slice (slices start at multiples of 16 rows).  Row rsub + 8 has the
 // swizzle of row rsub with bit 1 flipped, so its offset is the first one
-// XOR 32, plus 8 rows.
+// XOR 32, plus 8 rows.  tr_hi keeps the second offsets in registers up to
+// d = 128 and recomputes them at d = 256, where the dK pass has no
+// registers to spare.
 struct TrOffsets {
     int lo[4], hi[4];
 };
+template <class C>
+__device__ __forceinline__ int tr_hi(const TrOffsets &vo, int i) {
+    return C::D >= 256 ? (vo.lo[i] ^ 32) + 8 * C::RB : vo.hi[i];
+}
 template <class C>
 __device__ __forceinline__ TrOffsets tr_offsets(int lane) {
     const int h = lane >> 5;
@@ -96,7 +102,7 @@ __device__ __forceinline__ TrOffsets tr_offsets(int lane) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         t.lo[db] = rsub * C::RB + 16 * (4 * (db ^ (g >> 2)) + (y ^ (g & 3))) + 8 * (j & 1);
-        t.hi[db] = (t.lo[db] ^ 32) + 8 * C::RB;
+        t.hi[db] = C::D >= 256 ? 0 : (t.lo[db] ^ 32) + 8 * C::RB;
     }
     return t;
 }
@@ -198,7 +204,7 @@ __device__ __forceinline__ void pv_rows2(f32x16 (&o1)[C::DB], const char *blk1,
     auto rd = [&](const char *blk, int k2, int db) {
         const int base = 16 * k2 * C::RB + 256 * (db >> 2);
         const i16x4 lo = lds_read_tr16(blk + base + vo.lo[db & 3]);
-        const i16x4 hi = lds_read_tr16(blk + base + vo.hi[db & 3]);
+        const i16x4 hi = lds_read_tr16(blk + base + tr_hi<C>(vo, db & 3));
         return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 #pragma unroll
@@ -248,7 +254,7 @@ __device__ __forceinline__ void pv_rows1(f32x16 (&o)[C::DB], const char *blk,
         for (int db = 0; db < C::DB; ++db) {
             const char *base = blk + 16 * k2 * C::RB + 256 * (db >> 2);
             const i16x4 lo = lds_read_tr16(base + vo.lo[db & 3]);
-            const i16x4 hi = lds_read_tr16(base + vo.hi[db & 3]);
+            const i16x4 hi = lds_read_tr16(base + tr_hi<C>(vo, db & 3));
             a[k2][db] = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     __builtin_amdgcn_sched_barrier(0);
@@ -309,7 +315,7 @@ __device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs
         const int kb = i / (2 * C::DB), k2 = (i / C::DB) & 1, db = i % C::DB;
         const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + 256 * (db >> 2);
         const i16x4 lo = lds_read_tr16(base + vo.lo[db & 3]);
-        const i16x4 hi = lds_read_tr16(base + vo.hi[db & 3]);
+        const i16x4 hi = lds_read_tr16(base + tr_hi<C>(vo, db & 3));
         return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     v8 buf[L];
@@ -689,7 +695,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
             const int k2 = j / (2 * C::DB), db = (j >> 1) % C::DB;
             const char *base = ((j & 1) ? qt : gt) + (32 * blk + 16 * k2) * C::RB + 256 * (db >> 2);
             const i16x4 lo = lds_read_tr16(base + voff.lo[db & 3]);
-            const i16x4 hi = lds_read_tr16(base + voff.hi[db & 3]);
+            const i16x4 hi = lds_read_tr16(base + tr_hi<C>(voff, db & 3));
             return __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         auto load_stats = [&](int kb) {
