@@ -327,9 +327,15 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
             qk_tile<C>(s, kbuf(1 - PAR), koff, qf);
             schedule_qk<C>();
             if (masked) mask_tile<C>(s, (t + 1) * C::BC, rqi, n_kv, h);
+            // d = 64 (three waves per SIMD, bound by the softmax VALU): the
+            // wave in its PV + softmax section takes issue priority over the
+            // waves issuing S, so the exponentials of one wave keep flowing
+            // while another's S MFMAs fill the matrix core
+            if constexpr (C::D <= 64) __builtin_amdgcn_s_setprio(1);
             pv_tile<C>(o, vbuf(PAR), voff, pc);
             softmax_tile<C>(s, pn, m_use, l_acc, alpha, raised, c, dr, (t + 1) * C::BC);
             schedule_pv_softmax<C>();
+            if constexpr (C::D <= 64) __builtin_amdgcn_s_setprio(0);
         } else {
             pv_tile<C>(o, vbuf(PAR), voff, pc);
         }
