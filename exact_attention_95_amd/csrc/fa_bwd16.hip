@@ -438,7 +438,12 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         f32x16 s[C::KB], dp[C::KB];
         // reads ahead: as many as the register budget of two waves per SIMD allows
         constexpr int LQ = C::DROP && C::D >= 128 ? 4 : 6;
+        // the wave issuing S and dP takes issue priority over the other wave
+        // of its SIMD, which is then in its VALU or dQ part (measured +2 %
+        // at d = 128; no effect with one wave per SIMD)
+        __builtin_amdgcn_s_setprio(1);
         qk_dq_rolling<C, LQ>(s, dp, kbuf(PAR), vbuf(PAR), koff_k, koff_v, qf, gf);
+        __builtin_amdgcn_s_setprio(0);
         // keys past n_kv, and (causal) keys after qi, have P = 0
         const int lim = C::CAUSAL ? min(n_kv, qi + 1) : n_kv;
         v8 ds[C::KB][2];
