@@ -69,6 +69,33 @@ def test_args_struct_layout(tmp_path):
     assert got == want
 
 
+
+def test_headers_are_plain_c_and_the_library_links_from_c(tmp_path):
+    """Both public headers compile as strict C99 with no warnings, and a C
+    program links against libfa.so and calls its host-side entry points (no
+    GPU call: fa_validate and fa_strerror only)."""
+    src = tmp_path / "caller.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <string.h>\n#include "fa.h"\n#include "fa_probe.h"\n'
+        "int main(void) {\n"
+        "    fa_fwd_args a;\n"
+        "    memset(&a, 0, sizeof a);\n"
+        "    a.B = 1; a.H = 1; a.N_q = 4; a.N_kv = 4; a.d = 64; a.scale = 0.125f; a.dtype = FA_BF16;\n"
+        '    printf("%d\\n", fa_validate(&a));\n'
+        "    a.d = 96;\n"
+        '    printf("%d\\n", fa_validate(&a));\n'
+        '    printf("%s\\n", fa_strerror(FA_ERR_NULL));\n'
+        "    return 0;\n}\n")
+    exe = tmp_path / "caller"
+    lib_dir = os.path.dirname(fa.LIB_PATH)
+    cmd = ("gcc -std=c99 -Wall -Wextra -pedantic -Werror -I%s -o %s %s -L%s -lfa -Wl,-rpath,%s"
+           % (os.path.dirname(HEADER), exe, src, lib_dir, lib_dir))
+    assert os.system(cmd) == 0, cmd
+    out = os.popen(str(exe)).read().split("\n")
+    assert int(out[0]) == fa.FA_ERR_NULL      # required pointers missing
+    assert int(out[1]) == fa.FA_ERR_HEAD_DIM  # d = 96 is not compiled
+    assert out[2] == fa.fa_strerror(fa.FA_ERR_NULL)
+
 def good_args(**kw):
     a = fa.FaFwdArgs()
     a.Q, a.K, a.V, a.O, a.LSE = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000
