@@ -57,6 +57,33 @@ def test_small_shapes_match_oracle(idx):
     assert_within(w, err)
 
 
+
+def random_shapes(n: int, seed: int = 2024):
+    """n seeded random cases: every dtype, head dim and mask, with N_q and
+    N_kv drawn from 1..700 (mostly ragged against the 32-row waves and the
+    32/64-key tiles) and a few heads."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        dt = ["bf16", "f16", "f32", "fp8_e4m3"][int(rng.integers(0, 4))]
+        d = 128 if dt == "fp8_e4m3" else [64, 128, 256][int(rng.integers(0, 3))]
+        cases.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 701)),
+                      int(rng.integers(1, 701)), d, dt, bool(rng.integers(0, 2))))
+    return cases
+
+
+RANDOM = random_shapes(32)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM)), ids=["x".join(str(v) for v in c) for c in RANDOM])
+def test_random_shapes_match_oracle(idx):
+    B, H, nq, nkv, d, dt, causal = RANDOM[idx]
+    w, x = random_problem(700 + idx, B, H, nq, nkv, d, dt, causal)
+    say("case", RANDOM[idx])
+    err = full_parity(w, x=x)
+    say(err)
+    assert_within(w, err)
+
 def test_single_head_f32_workload():
     """The 1x1x256x64 float32 workload, whole tensor."""
     w = WORKLOADS["single_head_f32_n256_d64"]
