@@ -64,6 +64,31 @@ def test_bwd_matches_oracle(idx):
     assert_grads_within(errs, str(CASES[idx]))
 
 
+
+def random_bwd_shapes(n: int, seed: int = 2025):
+    """n seeded random cases: bf16 and fp16, every head dim and mask, N_q and
+    N_kv drawn from 1..500."""
+    rng = np.random.default_rng(seed)
+    return [(1, int(rng.integers(1, 3)), int(rng.integers(1, 501)), int(rng.integers(1, 501)),
+             [64, 128, 256][int(rng.integers(0, 3))], ["bf16", "f16"][int(rng.integers(0, 2))],
+             bool(rng.integers(0, 2))) for _ in range(n)]
+
+
+RANDOM = random_bwd_shapes(16)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM)), ids=["x".join(str(v) for v in c) for c in RANDOM])
+def test_bwd_random_shapes(idx):
+    B, H, nq, nkv, d, dt, causal = RANDOM[idx]
+    w, x = random_problem(450 + idx, B, H, nq, nkv, d, dt, causal)
+    dout = make_dout(w)
+    say("case", RANDOM[idx])
+    dq, dk, dv = run_bwd(w, x, dout)
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], dout, w.sm_scale, causal)
+    errs = {"dQ": grad_errors(to64(dq), rq), "dK": grad_errors(to64(dk), rk), "dV": grad_errors(to64(dv), rv)}
+    say(errs)
+    assert_grads_within(errs, str(RANDOM[idx]))
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
 def test_bwd_scales(scale):
     w, x = random_problem(420, 1, 2, 150, 190, 64, "bf16", True, scale=scale)
