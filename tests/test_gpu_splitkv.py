@@ -59,6 +59,31 @@ def test_splitkv_matches_oracle(idx):
     assert (l1 - lse).abs().max().item() <= 1e-3
 
 
+
+def random_split_shapes(n: int, seed: int = 2026):
+    """n seeded random cases: bf16 and fp16, d in {64, 128}, both masks, few
+    query rows (decode-like) against key ranges up to 5000, and chunk counts
+    from automatic (0) to more chunks than tiles (clamped)."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 65)), int(rng.integers(1, 5001)),
+             [64, 128][int(rng.integers(0, 2))], ["bf16", "f16"][int(rng.integers(0, 2))],
+             bool(rng.integers(0, 2)), [0, 1, 2, 7, 30, 1000][int(rng.integers(0, 6))]) for _ in range(n)]
+
+
+RANDOM = random_split_shapes(12)
+
+
+@pytest.mark.parametrize("idx", range(len(RANDOM)), ids=["x".join(str(v) for v in c) for c in RANDOM])
+def test_splitkv_random_shapes(idx):
+    B, H, nq, nkv, d, dt, causal, ns = RANDOM[idx]
+    w, x = random_problem(340 + idx, B, H, nq, nkv, d, dt, causal)
+    say("case", RANDOM[idx])
+    o, lse = run_split(w, x, ns)
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.sm_scale, causal)
+    err = errors(o.double().cpu().numpy(), lse.double().cpu().numpy(), o_ref, lse_ref)
+    say(err)
+    assert_within(w, err)
+
 def test_splitkv_errors():
     w, x = random_problem(320, 1, 1, 4, 256, 64, "bf16", False)
     q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
