@@ -669,10 +669,12 @@ def other_workloads(dev, seconds: float = 0.6) -> list:
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--gpus", type=int, default=1,
+                    help="number of GPUs; only 1 is supported (the path runs on one GPU)")
+    ap.add_argument("--steps", type=int, default=50, help="timed steps (one call over the whole batch each)")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before the timed region")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="workload name (default: %(default)s); see exact_attention_95_amd/inputs.py")
     ap.add_argument("--tile", type=int, default=0, help="fa_fwd_args.tile_override")
     ap.add_argument("--splitkv", type=int, default=None,
                     help="use the split-KV entry point with this many chunks (0: library "
@@ -682,7 +684,8 @@ def main(argv=None) -> int:
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability (Philox mask, seed 1, offset 0) for the forward "
                          "and --bwd runs")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle (and the parity check it carries)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
