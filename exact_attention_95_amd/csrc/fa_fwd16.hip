@@ -191,6 +191,20 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     __shared__ __attribute__((aligned(1024))) char sk1[C::TILE];
     __shared__ __attribute__((aligned(1024))) char sv0[C::TILE];
     __shared__ __attribute__((aligned(1024))) char sv1[C::TILE];
+    // Single pass, d <= 128: O leaves through LDS, so that global memory
+    // sees whole rows, 1 KB per store instruction, instead of 8-byte pieces
+    // of 32 rows (the MFMA accumulator layout).  At d = 64, Q arrives the
+    // same way, by direct-to-LDS copies of whole rows, into a buffer of its
+    // own (each wave owning 32 rows) that O reuses.  At d = 128 that buffer
+    // (64 KB) would leave LDS room for one workgroup per CU, and the
+    // compiler then schedules for that occupancy and spills; there O is
+    // staged in the tile buffers once every wave is done with them.  Rows
+    // use the K swizzle, which keeps the row-wise copies and reads and the
+    // column-wise operand reads and accumulator writes free of bank
+    // conflicts.  At d = 256 staging O measured slower.
+    constexpr bool STAGE_O = !C::SPLIT && C::D <= 128;
+    constexpr bool STAGE = STAGE_O && C::D <= 64;
+    __shared__ __attribute__((aligned(1024))) char sq[STAGE ? C::BR * C::RB : 16];
     auto kbuf = [&](int i) { return i ? sk1 : sk0; };
     auto vbuf = [&](int i) { return i ? sv1 : sv0; };
 
@@ -243,6 +257,19 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
 
     const CopyPlan<C, kLayoutK> kplan(w, lane);
     const CopyPlan<C, kLayoutV> vplan(w, lane);
+    char *qst = sq + (STAGE ? w * 32 * C::RB : 0);  // this wave's rows of Q, then of O
+    if constexpr (STAGE) {
+        // rows past n_q (a ragged last block) repeat the last row
+        const int qr0 = min(wq0, n_q - 1);
+        const int avail = min(n_q - qr0, 32);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(qh + (int64_t)qr0 * C::RB, avail * C::RB);
+#pragma unroll
+        for (int i = 0; i < C::RB / 32; ++i) {
+            const int r = (64 * i + lane) / C::NC, pc = lane % C::NC;
+            const int gr = min(r, avail - 1);
+            copy16_to_lds(rs, (unsigned)(gr * C::RB + 16 * (pc ^ kswz<C>(r))), qst + 1024 * i);
+        }
+    }
     if (ntile > 0) {
         kplan.issue(kh, 0, n_kv, kbuf(0), w, lane);
         vplan.issue(vh, 0, n_kv, vbuf(0), w, lane);
@@ -251,7 +278,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
 
     // ---- Q^T operand: lane holds Q[qi][ks*16 + 8h .. +7] for every k-step ----
     v8 qf[C::KS];
-    {
+    if constexpr (!STAGE) {
         const int qr = qi < n_q ? qi : n_q - 1;
         const char *qrow = qh + (int64_t)qr * C::RB + 16 * h;
 #pragma unroll
@@ -292,6 +319,14 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
 
     wait_vm();
     __syncthreads();
+    if constexpr (STAGE) {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            u32x4 raw = *(const u32x4 *)(qst + l32 * C::RB + 16 * ((2 * ks + h) ^ kswz<C>(l32)));
+            if (p.neg) raw ^= 0x80008000u;
+            qf[ks] = __builtin_bit_cast(v8, raw);
+        }
+    }
     if (wn > 0) {
         f32x16 s[C::KB];
         qk_tile<C>(s, kbuf(0), koff, qf);
@@ -348,9 +383,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     }
 
     // ---- epilogue: O = O_acc / l, LSE = m + ln l ----
-    if (qi >= n_q) return;
-    const float l_tot = sum_halves(l_acc);
     if (C::SPLIT) {
+        if (qi >= n_q) return;
+        const float l_tot = sum_halves(l_acc);
         // partial of this key chunk, float32; a row that sees no key of the
         // chunk (causal) gets O = 0 and LSE = -inf, i.e. weight 0 in the merge
         const int64_t row = ((int64_t)split * p.n_bh + bh) * n_q + qi;
@@ -368,8 +403,38 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
         if (h == 0) p.part_lse[row] = l_tot > 0.f ? (m_use + __log2f(l_tot)) * kLn2 : kNegInf;
         return;
     }
+    if (!STAGE_O) {
+        if (qi >= n_q) return;
+        const float l_tot = sum_halves(l_acc);
+        const float inv = p.o_mul / l_tot;
+        char *orow = p.o + ((int64_t)bh * n_q + qi) * C::RB;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                v4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = (T)(o[db][4 * jj + e] * inv);
+                *(v4 *)(orow + 2 * (32 * db + 8 * jj + 4 * h)) = out;
+            }
+        if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
+        return;
+    }
+    // O leaves through 32 staging rows of this wave: written by column from
+    // the accumulator layout, read back by row.  Without a buffer of its own
+    // the wave uses part of the tile buffers, after a barrier that lets the
+    // slowest wave finish its last reads of K and V.
+    static_assert(STAGE || C::SPLIT || C::BR <= 4 * C::BC, "O staging must fit the four tile buffers");
+    char *stage = qst;
+    if constexpr (!STAGE) {
+        __syncthreads();
+        constexpr int WPB = C::BC / 32;  // waves per tile buffer
+        const int b = w / WPB;
+        stage = (b == 0 ? sk0 : b == 1 ? sk1 : b == 2 ? sv0 : sv1) + (w % WPB) * 32 * C::RB;
+    }
+    if (wq0 >= n_q) return;
+    const float l_tot = sum_halves(l_acc);
     const float inv = p.o_mul / l_tot;
-    char *orow = p.o + ((int64_t)bh * n_q + qi) * C::RB;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -377,9 +442,20 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
             v4 out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) out[e] = (T)(o[db][4 * jj + e] * inv);
-            *(v4 *)(orow + 2 * (32 * db + 8 * jj + 4 * h)) = out;
+            *(v4 *)(stage + l32 * C::RB + 16 * ((4 * db + jj) ^ kswz<C>(l32)) + 8 * h) = out;
         }
-    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
+    if (p.lse && h == 0 && qi < n_q) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
+    // read back whole rows: NC lanes per row, 16 bytes each, so every store
+    // instruction writes 64 / NC consecutive rows, one contiguous kilobyte
+    constexpr int RPS = 64 / C::NC;
+    const int rr = lane / C::NC, cc = lane % C::NC;
+    char *obase = p.o + ((int64_t)bh * n_q + wq0) * C::RB;
+#pragma unroll
+    for (int s = 0; s < 32 / RPS; ++s) {
+        const int r = s * RPS + rr;
+        const u32x4 val = *(const u32x4 *)(stage + r * C::RB + 16 * (cc ^ kswz<C>(r)));
+        if (wq0 + r < n_q) *(u32x4 *)(obase + (int64_t)r * C::RB + 16 * cc) = val;
+    }
 }
 
 template <class C>
