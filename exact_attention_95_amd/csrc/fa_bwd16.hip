@@ -501,7 +501,19 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         else
             tile(p0, part, t);
     }
-    if (qi < n_q) store_rows<C>(p.dq + ((int64_t)bh * n_q + qi) * C::RB, dq, p.scale, h);
+    if constexpr (C::D <= 128) {
+        // dQ leaves through LDS as whole rows (store_rows_staged), in the
+        // tile buffers once every wave is past its last read of K and V
+        static_assert(C::BR <= 4 * C::BC, "dQ staging must fit the four tile buffers");
+        __syncthreads();
+        if (wq0 >= n_q) return;
+        constexpr int WPB = C::BC / 32;  // waves per tile buffer
+        const int b = w / WPB;
+        char *stage = (b == 0 ? sk0 : b == 1 ? sk1 : b == 2 ? sv0 : sv1) + (w % WPB) * 32 * C::RB;
+        store_rows_staged<C>(stage, p.dq + ((int64_t)bh * n_q + wq0) * C::RB, n_q - wq0, dq, p.scale, lane);
+    } else {
+        if (qi < n_q) store_rows<C>(p.dq + ((int64_t)bh * n_q + qi) * C::RB, dq, p.scale, h);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -826,7 +838,21 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
         if (t < tf) tile_rt(std::integral_constant<bool, false>(), t++);
     }
     for (; t < ntile; ++t) tile_rt(std::integral_constant<bool, true>(), t);
-    if (kj < n_kv) {
+    if constexpr (C::D <= 128) {
+        // dK and dV leave through LDS as whole rows (store_rows_staged), one
+        // after the other in the same staging rows of the tile buffers, once
+        // every wave is past its last read of Q and dO
+        static_assert(C::BR <= 4 * C::BC, "dK/dV staging must fit the four tile buffers");
+        __syncthreads();
+        if (wk0 >= n_kv) return;
+        constexpr int WPB = C::BC / 32;  // waves per tile buffer
+        const int b = w / WPB;
+        char *stage = (b == 0 ? sq0 : b == 1 ? sq1 : b == 2 ? sg0 : sg1) + (w % WPB) * 32 * C::RB;
+        const int64_t row0 = (int64_t)bh * n_kv + wk0;
+        if (C::WANT_DK) store_rows_staged<C>(stage, p.dk + row0 * C::RB, n_kv - wk0, dk, p.scale, lane);
+        if (C::WANT_DV)
+            store_rows_staged<C>(stage, p.dv + row0 * C::RB, n_kv - wk0, dv, C::DROP ? p.drop_scale : 1.f, lane);
+    } else if (kj < n_kv) {
         const int64_t row = (int64_t)bh * n_kv + kj;
         if (C::WANT_DK) store_rows<C>(p.dk + row * C::RB, dk, p.scale, h);
         if (C::WANT_DV) store_rows<C>(p.dv + row * C::RB, dv, C::DROP ? p.drop_scale : 1.f, h);

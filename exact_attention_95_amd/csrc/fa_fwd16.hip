@@ -420,10 +420,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
         if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
         return;
     }
-    // O leaves through 32 staging rows of this wave: written by column from
-    // the accumulator layout, read back by row.  Without a buffer of its own
-    // the wave uses part of the tile buffers, after a barrier that lets the
-    // slowest wave finish its last reads of K and V.
+    // O leaves through 32 staging rows of this wave.  Without a buffer of
+    // its own the wave uses part of the tile buffers, after a barrier that
+    // lets the slowest wave finish its last reads of K and V.
     static_assert(STAGE || C::SPLIT || C::BR <= 4 * C::BC, "O staging must fit the four tile buffers");
     char *stage = qst;
     if constexpr (!STAGE) {
@@ -434,28 +433,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
     }
     if (wq0 >= n_q) return;
     const float l_tot = sum_halves(l_acc);
-    const float inv = p.o_mul / l_tot;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            v4 out;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (T)(o[db][4 * jj + e] * inv);
-            *(v4 *)(stage + l32 * C::RB + 16 * ((4 * db + jj) ^ kswz<C>(l32)) + 8 * h) = out;
-        }
+    store_rows_staged<C>(stage, p.o + ((int64_t)bh * n_q + wq0) * C::RB, n_q - wq0, o, p.o_mul / l_tot, lane);
     if (p.lse && h == 0 && qi < n_q) p.lse[(int64_t)bh * n_q + qi] = (m_use + __log2f(l_tot)) * kLn2;
-    // read back whole rows: NC lanes per row, 16 bytes each, so every store
-    // instruction writes 64 / NC consecutive rows, one contiguous kilobyte
-    constexpr int RPS = 64 / C::NC;
-    const int rr = lane / C::NC, cc = lane % C::NC;
-    char *obase = p.o + ((int64_t)bh * n_q + wq0) * C::RB;
-#pragma unroll
-    for (int s = 0; s < 32 / RPS; ++s) {
-        const int r = s * RPS + rr;
-        const u32x4 val = *(const u32x4 *)(stage + r * C::RB + 16 * (cc ^ kswz<C>(r)));
-        if (wq0 + r < n_q) *(u32x4 *)(obase + (int64_t)r * C::RB + 16 * cc) = val;
-    }
 }
 
 template <class C>

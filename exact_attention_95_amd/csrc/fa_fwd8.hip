@@ -327,22 +327,43 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
         iteration(std::integral_constant<int, 1>(), t + 1, p1, p0);
     }
 
+    // O (bf16, 256-byte rows) leaves through LDS so that each store
+    // instruction writes 128-byte row segments instead of 8-byte pieces of
+    // 32 rows (the accumulator layout).  The tile buffers hold 4 KB per wave
+    // once every wave is past its last K/V read: 32 rows of 128 bytes, so
+    // each wave stages its rows in two column halves.  Staging rows of 128
+    // bytes use the swizzle (r / 2) % 8 of their 16-byte chunks, which keeps
+    // the 8-byte writes by column and the 16-byte reads by row free of bank
+    // conflicts.
+    static_assert(C::TILE == 2 * 4096 && C::NW == 8, "two waves' staging per tile buffer");
+    __syncthreads();
+    if (wq0 >= n_q) return;
     float lo, hi;
     both_halves8(l_acc, lo, hi);
     const float l_tot = lo + hi;
-    if (qi >= n_q) return;
     const float inv = p.o_mul / l_tot;
-    char *orow = p.o + ((int64_t)bh * n_q + qi) * (2 * C::D);
+    char *stage = (w < 2 ? sk0 : w < 4 ? sk1 : w < 6 ? sv0 : sv1) + 4096 * (w & 1);
+    const int rr = lane >> 3, cc = lane & 7;
+    char *obase = p.o + ((int64_t)bh * n_q + wq0) * (2 * C::D);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            bf16x4 out;
+        for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) out[e] = (__bf16)(o[db][4 * jj + e] * inv);
-            *(bf16x4 *)(orow + 2 * (32 * db + 8 * jj + 4 * h)) = out;
+            for (int jj = 0; jj < 4; ++jj) {
+                bf16x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = (__bf16)(o[2 * half + d2][4 * jj + e] * inv);
+                *(bf16x4 *)(stage + 128 * l32 + 16 * ((4 * d2 + jj) ^ ((l32 >> 1) & 7)) + 8 * h) = out;
+            }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int r = 8 * s4 + rr;
+            const u32x4 val = *(const u32x4 *)(stage + 128 * r + 16 * (cc ^ ((r >> 1) & 7)));
+            if (wq0 + r < n_q) *(u32x4 *)(obase + (int64_t)r * (2 * C::D) + 128 * half + 16 * cc) = val;
         }
-    if (p.lse && h == 0) p.lse[(int64_t)bh * n_q + qi] = (m_use - C::PSHIFT + __log2f(l_tot)) * kLn2;
+    }
+    if (p.lse && h == 0 && qi < n_q) p.lse[(int64_t)bh * n_q + qi] = (m_use - C::PSHIFT + __log2f(l_tot)) * kLn2;
 }
 
 template <class C>

@@ -99,6 +99,38 @@ struct CopyPlan {
     }
 };
 
+// Stores the 32 rows of an O^T-layout accumulator (one row per lane, d
+// columns), times mul and converted to T, through 32 staging rows of LDS
+// that belong to this wave: written by column in the K swizzle, read back by
+// row, so that every store instruction writes 64 / NC consecutive whole rows
+// (one kilobyte) instead of 8-byte pieces of 32 rows.  The K swizzle keeps
+// the 8-byte writes and the 16-byte reads free of bank conflicts.  Rows at or
+// past `valid` are not stored.
+template <class C>
+__device__ __forceinline__ void store_rows_staged(char *stage, char *dst, int valid, const f32x16 (&acc)[C::DB],
+                                                  float mul, int lane) {
+    typedef typename Mma16<typename C::T>::v4 v4;
+    typedef typename C::T T;
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            v4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = (T)(acc[db][4 * jj + e] * mul);
+            *(v4 *)(stage + l32 * C::RB + 16 * ((4 * db + jj) ^ kswz<C>(l32)) + 8 * h) = out;
+        }
+    constexpr int RPS = 64 / C::NC;  // rows per store instruction
+    const int rr = lane / C::NC, cc = lane % C::NC;
+#pragma unroll
+    for (int s = 0; s < 32 / RPS; ++s) {
+        const int r = s * RPS + rr;
+        const u32x4 val = *(const u32x4 *)(stage + r * C::RB + 16 * (cc ^ kswz<C>(r)));
+        if (r < valid) *(u32x4 *)(dst + (int64_t)r * C::RB + 16 * cc) = val;
+    }
+}
+
 // v_permlane32_swap(a, b) returns ([a_lo, b_lo], [a_hi, b_hi]) (lo = lanes
 // 0-31, hi = lanes 32-63).  With a = b = x every lane thus receives the lower
 // half's x in the first result and the upper half's x in the second.  The
