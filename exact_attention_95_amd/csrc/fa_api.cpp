@@ -100,7 +100,7 @@ int validate_fwd_common(const fa_fwd_args *a) {
     if (!isfinite((float)score_factor(a))) return FA_ERR_SCALE;
     const int p8 = dropout_p8(a->dropout_p);
     if (p8 < 0) return FA_ERR_DROPOUT;
-    if (p8 > 0 && ((a->dtype != FA_BF16 && a->dtype != FA_F16) || a->d > 128)) return FA_ERR_DROPOUT;
+    if (p8 > 0 && a->dtype != FA_BF16 && a->dtype != FA_F16) return FA_ERR_DROPOUT;
     if (fa_num_variants(a->dtype, a->d, a->causal) == 0) return FA_ERR_HEAD_DIM;
     if (a->tile_override < 0 || a->tile_override > fa_num_variants(a->dtype, a->d, a->causal))
         return FA_ERR_VARIANT;
@@ -166,7 +166,7 @@ extern "C" const char *fa_strerror(int status) {
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_VARIANT: return "no compiled variant for this problem (or tile_override out of range)";
         case FA_ERR_WORKSPACE: return "workspace NULL, misaligned or too small";
-        case FA_ERR_DROPOUT: return "dropout_p outside [0, 1), or dropout not supported here (fp16/bf16, d <= 128, not split-KV)";
+        case FA_ERR_DROPOUT: return "dropout_p outside [0, 1), or dropout not supported here (fp16/bf16 only, not split-KV)";
         case FA_ERR_LONG_KV: return "N_kv above the single-pass limit of 2^20 keys per row; use fa_fwd_splitkv";
         case FA_ERR_SCRATCH: return "split-KV partials exceed the 64 MiB static scratch buffer of fa_fwd_splitkv_noalloc; use fa_fwd_splitkv with a workspace";
         default: return "unknown status";
@@ -396,8 +396,6 @@ extern "C" int fa_bwd_validate(const fa_bwd_args *a) {
         return FA_ERR_SCALE;
     const int p8 = dropout_p8(a->dropout_p);
     if (p8 < 0) return FA_ERR_DROPOUT;
-    // dropout instances exist for d <= 128, as in the forward
-    if (p8 > 0 && a->d > 128) return FA_ERR_DROPOUT;
     if (!find_bwd(a->dtype, a->d, a->causal)) return FA_ERR_HEAD_DIM;
     if (bh == 0) return FA_OK;  // nothing to read or write
     if (!a->K || !a->V || !a->dK || !a->dV) return FA_ERR_NULL;

@@ -48,8 +48,9 @@ __device__ __forceinline__ void static_for(F &&f) {
     static_for_impl(f, std::make_integer_sequence<int, N>());
 }
 
-// DROP: the dropout keep mask of the forward is replayed.  PART (dK/dV
-// kernel): 0 accumulates dK and dV, 1 dV only, 2 dK only.
+// DROP: the dropout keep mask of the forward is replayed.  PART: in the
+// dK/dV kernel 0 accumulates dK and dV, 1 dV only, 2 dK only; in the dQ
+// kernel 0 accumulates all of dQ, 1 its first half of columns, 2 the second.
 template <typename T_, int D_, int NW_, bool CAUSAL_, bool DROP_ = false, int PART_ = 0>
 struct CfgB {
     typedef T_ T;
@@ -62,6 +63,8 @@ struct CfgB {
     static constexpr int TILE = BC * RB;
     static constexpr int KS = D / 16, KB = BC / 32, DB = D / 32, LDI = TILE / (1024 * NW);
     static constexpr int NVO = DB < 4 ? DB : 4;
+    // dQ column blocks of this pass (dQ kernel)
+    static constexpr int QDB = PART_ == 0 ? DB : DB / 2, QDB0 = PART_ == 2 ? DB / 2 : 0;
     static constexpr int LDS = 4 * TILE + 2 * 512;  // two streams x two buffers, + LSE/D tiles
     // waves per SIMD the register budget must allow: at d = 64 the dK/dV
     // kernel fits two (two workgroups of 4 waves per CU); at d = 128 its
@@ -121,12 +124,13 @@ __device__ __forceinline__ void load_rows(const char *base, int row, int n,
 
 // Stores rows of an O^T-layout accumulator (one row per lane, d columns)
 // times mul, converted to T.
-template <class C>
-__device__ __forceinline__ void store_rows(char *rowp, const f32x16 (&acc)[C::DB], float mul, int h) {
+template <class C, int NDB = C::DB, int DB0 = 0>
+__device__ __forceinline__ void store_rows(char *rowp, const f32x16 (&acc)[NDB], float mul, int h) {
     typedef typename Mma16<typename C::T>::v4 v4;
     typedef typename C::T T;
+    rowp += 64 * DB0;  // column 32 DB0
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             v4 out;
@@ -306,13 +310,14 @@ __device__ __forceinline__ void qk_dq_rolling(f32x16 (&s)[C::KB], f32x16 (&dp)[C
 // o^T += V_tile^T P^T as pv_tile, with a rolling window of L MFMAs' operand
 // reads (two transposed reads each) ahead.
 template <class C, int L>
-__device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs, const TrOffsets &vo,
+__device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::QDB], const char *Vs, const TrOffsets &vo,
                                               const typename Mma16<typename C::T>::v8 (&pb)[C::KB][2]) {
     typedef Mma16<typename C::T> M;
     typedef typename M::v8 v8;
-    constexpr int N = C::KB * 2 * C::DB;
+    constexpr int NB = C::QDB;  // column blocks C::QDB0 .. + NB of this pass
+    constexpr int N = C::KB * 2 * NB;
     auto rd = [&](int i) {
-        const int kb = i / (2 * C::DB), k2 = (i / C::DB) & 1, db = i % C::DB;
+        const int kb = i / (2 * NB), k2 = (i / NB) & 1, db = C::QDB0 + i % NB;
         const char *base = Vs + (kb * 32 + 16 * k2) * C::RB + 256 * (db >> 2);
         const i16x4 lo = lds_read_tr16(base + vo.lo[db & 3]);
         const i16x4 hi = lds_read_tr16(base + tr_hi<C>(vo, db & 3));
@@ -323,7 +328,7 @@ __device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::DB], const char *Vs
     for (int j = 0; j < L; ++j) buf[j] = rd(j);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        const int kb = i / (2 * C::DB), k2 = (i / C::DB) & 1, db = i % C::DB;
+        const int kb = i / (2 * NB), k2 = (i / NB) & 1, db = i % NB;
         o[db] = M::mma(buf[i % L], pb[kb][k2], o[db]);
         if (i + L < N) buf[i % L] = rd(i + L);
         __builtin_amdgcn_sched_barrier(0);
@@ -419,9 +424,9 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     const int koff_v = l32 * C::RB + 16 * (h ^ kswz<C>(l32));
     const TrOffsets voff = tr_offsets<C>(lane);
 
-    f32x16 dq[C::DB];
+    f32x16 dq[C::QDB];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) dq[db] = (f32x16){};
+    for (int db = 0; db < C::QDB; ++db) dq[db] = (f32x16){};
 
     // MASKED: the tile holds keys past n_kv or (causal) keys after some row
     // of this wave; only such tiles carry the compare and select per element
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
         char *stage = (b == 0 ? sk0 : b == 1 ? sk1 : b == 2 ? sv0 : sv1) + (w % WPB) * 32 * C::RB;
         store_rows_staged<C>(stage, p.dq + ((int64_t)bh * n_q + wq0) * C::RB, n_q - wq0, dq, p.scale, lane);
     } else {
-        if (qi < n_q) store_rows<C>(p.dq + ((int64_t)bh * n_q + qi) * C::RB, dq, p.scale, h);
+        if (qi < n_q) store_rows<C, C::QDB, C::QDB0>(p.dq + ((int64_t)bh * n_q + qi) * C::RB, dq, p.scale, h);
     }
 }
 
@@ -861,7 +866,14 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dkdv_kernel(BwdParams
 
 template <typename T, int D, int NWQ, int NWK, bool CAUSAL, bool DROP>
 int launch_bwd_t(const BwdParams &p, void *stream) {
-    typedef CfgB<T, D, NWQ, CAUSAL, DROP> CQ;
+    // d = 256 with dropout: the dQ kernel as two passes over the two halves
+    // of dQ's columns (each recomputes S and dP).  In one pass, the Philox
+    // state on top of the full dQ accumulator exceeds the 512 registers of a
+    // wave and spilled about 100 of them (3.2 times the time of the
+    // dropout-free kernel).
+    constexpr bool QSPLIT = D >= 256 && DROP;
+    typedef CfgB<T, D, NWQ, CAUSAL, DROP, (QSPLIT ? 1 : 0)> CQ;
+    typedef CfgB<T, D, NWQ, CAUSAL, DROP, 2> CQ2;
     // d = 256: the dK/dV kernel as two passes (dV, then dK), see above
     typedef CfgB<T, D, NWK, CAUSAL, DROP, (D >= 256 ? 1 : 0)> CK;
     typedef CfgB<T, D, NWK, CAUSAL, DROP, 2> CK2;
@@ -873,6 +885,7 @@ int launch_bwd_t(const BwdParams &p, void *stream) {
                            st, p);
         const int nq = (p.n_q + CQ::BR - 1) / CQ::BR;
         hipLaunchKernelGGL(bwd_dq_kernel<CQ>, dim3(p.n_bh * nq), dim3(CQ::NT), 0, st, p);
+        if constexpr (QSPLIT) hipLaunchKernelGGL(bwd_dq_kernel<CQ2>, dim3(p.n_bh * nq), dim3(CQ2::NT), 0, st, p);
     }
     const int nk = (p.n_kv + CK::BR - 1) / CK::BR;
     hipLaunchKernelGGL(bwd_dkdv_kernel<CK>, dim3(p.n_bh * nk), dim3(CK::NT), 0, st, p);
@@ -882,14 +895,8 @@ int launch_bwd_t(const BwdParams &p, void *stream) {
 
 template <typename T, int D, int NWQ, int NWK, bool CAUSAL>
 int launch_bwd(const BwdParams &p, void *stream) {
-    if constexpr (D >= 256) {
-        // no dropout instances at d = 256 (the forward has none either;
-        // fa_bwd_validate refuses it)
-        return p.p8 != 0 ? 1 : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
-    } else {
-        return p.p8 != 0 ? launch_bwd_t<T, D, NWQ, NWK, CAUSAL, true>(p, stream)
-                         : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
-    }
+    return p.p8 != 0 ? launch_bwd_t<T, D, NWQ, NWK, CAUSAL, true>(p, stream)
+                     : launch_bwd_t<T, D, NWQ, NWK, CAUSAL, false>(p, stream);
 }
 
 // The dropout keep mask as bytes, one 4 x 4 block of one slice per thread

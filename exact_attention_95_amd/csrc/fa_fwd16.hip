@@ -440,8 +440,8 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd16_kernel(KParams p) {
 template <class C>
 int launch(const KParams &p, void *stream) {
     if (p.p8 != 0) {
-        // dropout instances exist for the single-pass kernels with d <= 128
-        if constexpr (!C::SPLIT && C::D <= 128) {
+        // dropout instances exist for the single-pass kernels
+        if constexpr (!C::SPLIT) {
             hipLaunchKernelGGL(fwd16_kernel<typename C::WithDrop>, dim3(p.n_wg), dim3(C::NT), 0,
                                (hipStream_t)stream, p);
             return hipGetLastError() == hipSuccess ? 0 : 1;

@@ -125,8 +125,8 @@ int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
  * (dropout_seed mod 2^32, dropout_seed / 2^32) is >= p8; byte k of the four
  * output words w0..w3 is bits 8 (k mod 4) .. +7 of word k / 4.  i and j are
  * the row and key indices within the (batch, head).  Supported for FA_F16
- * and FA_BF16 with d in {64, 128} and the default tile (tile_override 0 or
- * 1); FA_ERR_DROPOUT otherwise, and from fa_fwd_splitkv.  fa_bwd with the
+ * and FA_BF16 (every d and tile variant); FA_ERR_DROPOUT for other dtypes
+ * and from fa_fwd_splitkv.  fa_bwd with the
  * same dropout_p, dropout_seed and dropout_offset replays the same mask.
  * fa_dropout_mask writes the mask itself.
  */
@@ -230,8 +230,8 @@ int64_t fa_splitkv_workspace_bytes(const fa_fwd_args *args, int num_splits);
  * type.  dQ, dK, dV: device outputs with the type and layout of Q, K and V,
  * written in full; they must not overlap each other, the inputs or the
  * workspace (FA_ERR_ALIAS).  dtype: FA_BF16 or FA_F16 (else FA_ERR_DTYPE); d
- * in {64, 128, 256} (else FA_ERR_HEAD_DIM); dropout with d <= 128 only (as
- * in the forward; FA_ERR_DROPOUT otherwise).  Other rules as for fa_fwd_ex (shapes,
+ * in {64, 128, 256} (else FA_ERR_HEAD_DIM); dropout as in the forward.
+ * Other rules as for fa_fwd_ex (shapes,
  * 16-byte alignment, finite scale, top-left causal mask).  B or H equal to 0
  * is a no-op; N_q = 0 writes dK = dV = 0.
  */

@@ -312,7 +312,6 @@ def test_bwd_validate_accepts_good_args():
     (dict(dtype=9), fa.FA_ERR_DTYPE),
     (dict(d=96), fa.FA_ERR_HEAD_DIM),
     (dict(d=512), fa.FA_ERR_HEAD_DIM),
-    (dict(d=256, dropout_p=0.1), fa.FA_ERR_DROPOUT),
     (dict(d=96), fa.FA_ERR_HEAD_DIM),
     (dict(N_kv=0), fa.FA_ERR_SHAPE),
     (dict(B=-1), fa.FA_ERR_SHAPE),
@@ -374,7 +373,7 @@ def test_dropout_support_limits():
     assert fa.fa_validate(good_args(dropout_p=0.1)) == fa.FA_OK
     assert fa.fa_validate(good_args(dropout_p=0.1, dtype=fa.FA_F16, d=128, causal=1)) == fa.FA_OK
     assert fa.fa_validate(good_args(dropout_p=0.1, dtype=fa.FA_F32)) == fa.FA_ERR_DROPOUT
-    assert fa.fa_validate(good_args(dropout_p=0.1, d=256)) == fa.FA_ERR_DROPOUT
+    assert fa.fa_validate(good_args(dropout_p=0.1, d=256)) == fa.FA_OK
     assert fa.fa_validate(good_args(dropout_p=0.1, dtype=fa.FA_FP8_E4M3, d=128)) == fa.FA_ERR_DROPOUT
     # p quantised to 0 (p < 1/512) is no dropout, accepted everywhere
     assert fa.fa_validate(good_args(dropout_p=1e-4, dtype=fa.FA_F32)) == fa.FA_OK
@@ -383,9 +382,9 @@ def test_dropout_support_limits():
     assert fa.fa_splitkv_workspace_bytes(a, 0) == -1
     assert fa.fa_fwd_splitkv(a, 0, None, 0) == fa.FA_ERR_DROPOUT
     assert fa.fa_bwd_validate(good_bwd_args(dropout_p=0.3, dropout_seed=2**64 - 1, dropout_offset=7)) == fa.FA_OK
-    # d = 256: the backward runs without dropout only, as the forward
     assert fa.fa_bwd_validate(good_bwd_args(d=256)) == fa.FA_OK
-    assert fa.fa_bwd_validate(good_bwd_args(d=256, dropout_p=0.2)) == fa.FA_ERR_DROPOUT
+    assert fa.fa_bwd_validate(good_bwd_args(d=256, dropout_p=0.2)) == fa.FA_OK
+    assert fa.fa_bwd_validate(good_bwd_args(d=256, dropout_p=0.2, dtype=fa.FA_F32)) == fa.FA_ERR_DTYPE
 
 
 def test_dropout_mask_entry_validation():

@@ -38,6 +38,8 @@ CASES = [
     (2, 1, 333, 333, 128, "bf16", True, 0.2),
     (1, 2, 130, 257, 128, "f16", False, 0.5),
     (1, 1, 300, 100, 64, "f16", True, 0.3),
+    (1, 2, 160, 200, 256, "bf16", False, 0.2),
+    (1, 1, 291, 291, 256, "f16", True, 0.1),
 ]
 
 
