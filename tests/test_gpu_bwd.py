@@ -179,3 +179,30 @@ def test_bwd_full_size_sampled(name):
     errs = {"dQ": grad_errors(gq, rq), "dK": grad_errors(gk, rk), "dV": grad_errors(gv, rv)}
     say(name, rows.size, keys.size, errs)
     assert_grads_within(errs, name)
+
+
+@pytest.mark.parametrize("d,dt,causal", [(64, "bf16", True), (128, "f16", False), (256, "bf16", True)])
+def test_bwd_no_write_past_end(d, dt, causal):
+    """dQ, dK and dV of ragged last blocks (77 query rows, 90 keys) stop at
+    their tensors' ends (whole-row stores from LDS staging rows are masked by
+    row) and equal the binding's own result, through the C ABI."""
+    w, x = random_problem(17, 1, 2, 77, 90, d, dt, causal)
+    q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, scale=w.sm_scale, causal=causal)
+    do = make_dout(w).cuda()
+    ref = fa.bwd(q, k, v, o, lse, do, scale=w.sm_scale, causal=causal)
+    guards, outs = [], []
+    for t in (q, k, v):
+        n = t.numel()
+        g = torch.full((n + 8192,), 7.0, dtype=t.dtype, device="cuda")
+        guards.append((g, n))
+        outs.append(g[:n].view(t.shape))
+    stream = fa._stream_handle(None, q.device)
+    a = fa.make_bwd_args(q, k, v, o, lse, do, *outs, w.sm_scale, causal, stream)
+    need = fa.fa_bwd_workspace_bytes(a)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    assert fa.fa_bwd(a, ws.data_ptr(), ws.numel()) == fa.FA_OK
+    torch.cuda.synchronize()
+    for (g, n), got, want in zip(guards, outs, ref):
+        assert torch.all(g[n:] == 7.0)
+        assert torch.equal(got, want)

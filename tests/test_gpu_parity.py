@@ -165,14 +165,20 @@ def test_huge_logits_stay_finite():
     assert_within(w, err)
 
 
-def test_lse_optional_and_no_write_past_end():
-    w, x = random_problem(16, 1, 2, 77, 90, 64, "bf16", False)
+@pytest.mark.parametrize("d,dt,causal", [(64, "bf16", False), (128, "f16", True), (256, "bf16", False),
+                                         (128, "fp8_e4m3", False)])
+def test_lse_optional_and_no_write_past_end(d, dt, causal):
+    """O of a ragged last query block (77 rows) stops at the tensor's end:
+    whole-row stores from the LDS staging rows are masked by row."""
+    w, x = random_problem(16, 1, 2, 77, 90, d, dt, causal)
     q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
-    guard = torch.full((2 * 77 * 64 + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
-    out = guard[:2 * 77 * 64].view(1, 2, 77, 64)
-    fa.fwd(q, k, v, scale=w.sm_scale, out=out, with_lse=False)
+    n = 2 * 77 * d
+    odt = torch.bfloat16 if dt == "fp8_e4m3" else q.dtype
+    guard = torch.full((n + 8192,), 7.0, dtype=odt, device="cuda")
+    out = guard[:n].view(1, 2, 77, d)
+    fa.fwd(q, k, v, scale=w.sm_scale, causal=causal, descale=x["descale"], out=out, with_lse=False)
     torch.cuda.synchronize()
-    assert torch.all(guard[2 * 77 * 64:] == 7.0)
+    assert torch.all(guard[n:] == 7.0)
     o_ref, _ = run_gpu(w, x)
     assert torch.equal(out, o_ref)
 
