@@ -521,9 +521,11 @@ def power_check(w, step, inputs, stream, flops: float, refresh=None, pass_name: 
 
 
 def hbm_reference(dev, nbytes: int = 4 << 30, reps: int = 10) -> dict:
-    """GB/s of torch's device copy (bytes read + written) and of a float32 sum
-    over bf16 data (bytes read), each on `nbytes` of input."""
+    """GB/s of the library's streaming-read probe (fa_probe_hbm_read, 8192
+    workgroups), of torch's device copy (bytes read + written) and of a
+    float32 sum over bf16 data (bytes read), each on `nbytes` of input."""
     import torch
+    from exact_attention_95_amd import fa
     x = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
     y = torch.empty_like(x)
     acc = torch.empty((), dtype=torch.float32, device=dev)
@@ -540,7 +542,17 @@ def hbm_reference(dev, nbytes: int = 4 << 30, reps: int = 10) -> dict:
         torch.cuda.synchronize()
         return round(moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
 
+    n_wg = 8192
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+
+    def probe():
+        st = fa.fa_probe_hbm_read(x.data_ptr(), nbytes, n_wg, sink.data_ptr(),
+                                  torch.cuda.current_stream(dev).cuda_stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
     rec = {"bytes": nbytes,
+           "read_probe_GBps": rate(probe, nbytes),
            "copy_GBps": rate(lambda: y.copy_(x), 2 * nbytes),
            "sum_read_GBps": rate(lambda: acc.copy_(x.sum(dtype=torch.float32)), nbytes)}
     del x, y
@@ -918,12 +930,17 @@ def main(argv=None) -> int:
                      "kernel_ms": round(kernel_ms, 4)},
     }
     if extras and hbm_bound:
-        # what torch's own streaming kernels reach on this HBM, for scale: a
-        # device copy (read + write) and a float32 sum (read), 4 GiB each
+        # what plain streaming reaches on this HBM, for scale: the library's
+        # read probe, torch's device copy (read + write) and a float32 sum
+        # (read), 4 GiB each
         extras["hbm_reference"] = hbm_reference(dev)
     if extras:
         rec.update(extras)
-        if not hbm_bound:
+        if hbm_bound:
+            # the kernel's rate against the read rate measured on this device
+            rec["roofline"]["frac_of_measured_peak"] = round(
+                achieved / extras["hbm_reference"]["read_probe_GBps"], 4)
+        else:
             # the kernel's rate against the MFMA rate measured on this device
             rec["roofline"]["frac_of_measured_peak"] = round(
                 achieved / extras["device"]["mfma_tflops"], 4)

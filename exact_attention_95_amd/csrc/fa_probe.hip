@@ -129,6 +129,27 @@ __global__ __launch_bounds__(kThreads) void valu_probe_kernel(int64_t iters, flo
     sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// Streaming read of n16 16-byte chunks at a: thread t of the T threads of
+// the grid reads chunks t, t + T, t + 2T, ..., eight at a time in flight
+// (non-temporal: the data is read once), and stores the low 16 bits of the
+// xor of the words it read, as an exact float.
+__global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4 *__restrict__ a, int64_t n16, float *sink) {
+    constexpr int U = 8;
+    const int64_t T = (int64_t)gridDim.x * kThreads;
+    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (; i + (U - 1) * T < n16; i += U * T) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(a + i + u * T);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+    for (; i < n16; i += T) acc ^= __builtin_nontemporal_load(a + i);
+    const unsigned x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = (float)(x & 0xFFFFu);
+}
+
 bool on_gfx950() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
@@ -158,6 +179,17 @@ extern "C" int64_t fa_probe_wall_clock_khz(void) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
     if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
     return khz > 0 ? khz : 0;
+}
+
+extern "C" int fa_probe_hbm_read(const void *buf, int64_t bytes, int64_t n_wg, float *sink, void *stream) {
+    using namespace fa;
+    if (n_wg < 1 || n_wg > (1 << 20) || bytes < 16 || bytes % 16) return FA_ERR_SHAPE;
+    if (!buf || !sink) return FA_ERR_NULL;
+    if ((uintptr_t)buf % 16 || (uintptr_t)sink % alignof(float)) return FA_ERR_ALIGN;
+    if (!on_gfx950()) return FA_ERR_DEVICE;
+    hipLaunchKernelGGL(hbm_read_kernel, dim3((unsigned)n_wg), dim3(kThreads), 0, (hipStream_t)stream,
+                       (const u32x4 *)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" int fa_probe(int kind, int64_t n_wg, int64_t iters, float *sink, uint64_t *clocks, void *stream) {

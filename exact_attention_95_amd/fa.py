@@ -4,7 +4,7 @@ The functions ``fa_fwd``, ``fa_fwd_ex``, ``fa_validate``, ``fa_strerror``,
 ``fa_num_variants``, ``fa_variant_name``, ``fa_fwd_splitkv``,
 ``fa_splitkv_workspace_bytes``, ``fa_bwd``, ``fa_bwd_validate``,
 ``fa_bwd_workspace_bytes``, ``fa_dropout_mask``, ``fa_fwd_splitkv_noalloc`` and the measurement probes
-``fa_probe``, ``fa_probe_work_per_iter`` and ``fa_probe_wall_clock_khz``
+``fa_probe``, ``fa_probe_hbm_read``, ``fa_probe_work_per_iter`` and ``fa_probe_wall_clock_khz``
 (include/fa_probe.h) mirror the C entry points of the same names.  ``fwd``
 is the torch convenience form: it allocates O and LSE with torch on the
 inputs' device and calls ``fa_fwd_ex`` on torch's current stream.  All attention arithmetic runs in the HIP kernels; there is no CPU
@@ -30,7 +30,7 @@ EXPORTED = ("fa_fwd", "fa_fwd_ex", "fa_validate", "fa_strerror", "fa_num_variant
             "fa_variant_name", "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_bwd",
             "fa_bwd_validate", "fa_bwd_workspace_bytes", "fa_dropout_mask", "fa_fwd_splitkv_noalloc")
 # measurement probes (include/fa_probe.h)
-PROBE_EXPORTED = ("fa_probe", "fa_probe_work_per_iter", "fa_probe_wall_clock_khz")
+PROBE_EXPORTED = ("fa_probe", "fa_probe_hbm_read", "fa_probe_work_per_iter", "fa_probe_wall_clock_khz")
 (FA_PROBE_MFMA_BF16, FA_PROBE_MFMA_F16, FA_PROBE_MFMA_FP8, FA_PROBE_MFMA_F32, FA_PROBE_EXP,
  FA_PROBE_FMA) = range(6)
 
@@ -118,6 +118,8 @@ def load(path: str = LIB_PATH):
                                             i64, vp, vp]
             lib.fa_probe.restype = ctypes.c_int
             lib.fa_probe.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp]
+            lib.fa_probe_hbm_read.restype = ctypes.c_int
+            lib.fa_probe_hbm_read.argtypes = [vp, i64, i64, vp, vp]
             lib.fa_probe_work_per_iter.restype = ctypes.c_double
             lib.fa_probe_work_per_iter.argtypes = [ctypes.c_int]
             lib.fa_probe_wall_clock_khz.restype = i64
@@ -182,6 +184,10 @@ def fa_dropout_mask(dropout_p, seed, offset, BH, N_q, N_kv, mask, stream=None) -
 
 def fa_probe(kind, n_wg, iters, sink, clocks=None, stream=None) -> int:
     return load().fa_probe(kind, n_wg, iters, sink, clocks, stream)
+
+
+def fa_probe_hbm_read(buf, nbytes, n_wg, sink, stream=None) -> int:
+    return load().fa_probe_hbm_read(buf, nbytes, n_wg, sink, stream)
 
 
 def fa_probe_work_per_iter(kind) -> float:

@@ -9,8 +9,10 @@
  * close a kernel gets, these probes measure on the device itself what the
  * published peaks only assume: the sustained MFMA rate of each input type,
  * the rate of v_exp_f32 and of a plain fp32 FMA, and the shader clock while
- * they run.  Each probe is one kernel of register-only loops with many
- * independent dependency chains per wave.
+ * they run.  Each kind of fa_probe is one kernel of register-only loops with
+ * many independent dependency chains per wave.  The split-KV decode is bound
+ * by HBM instead; fa_probe_hbm_read measures the read rate it is held
+ * against.
  *
  * Memory.  sink and clocks are device buffers owned by the caller:
  * sink holds n_wg * 256 floats (one result per thread, written so that the
@@ -20,9 +22,18 @@
  * clocks may be NULL).  Workgroups have 256 threads (4 waves).  The call is
  * asynchronous on stream (hipStream_t, NULL = null stream).
  *
+ * fa_probe_hbm_read measures the other bound, HBM: a streaming read of the
+ * caller's device buffer buf (bytes, a multiple of 16, 16-byte aligned;
+ * read only).  Its n_wg workgroups of 256 threads read the buffer's 16-byte
+ * chunks grid-stride, eight loads in flight per thread, and each thread
+ * stores the low 16 bits of the xor of the 32-bit words it read (as an exact
+ * float) into sink[n_wg * 256].  bytes / (time of the call) is the read rate
+ * that a kernel bound by HBM reads is compared with.
+ *
  * Errors.  0 (FA_OK); FA_ERR_SHAPE for n_wg outside [1, 2^20] or iters outside
- * [1, 2^30]; FA_ERR_NULL for a NULL sink; FA_ERR_ALIGN for a sink not 4-byte
- * or clocks not 8-byte aligned; FA_ERR_DTYPE for an unknown kind;
+ * [1, 2^30] (fa_probe_hbm_read: bytes not a positive multiple of 16); FA_ERR_NULL
+ * for a NULL sink or buf; FA_ERR_ALIGN for a sink not 4-byte, clocks not
+ * 8-byte or buf not 16-byte aligned; FA_ERR_DTYPE for an unknown kind;
  * FA_ERR_DEVICE without a gfx950 device; FA_ERR_LAUNCH if the launch fails.
  */
 #ifndef FA_PROBE_H_
@@ -45,6 +56,9 @@ typedef enum {
 
 /* Runs probe `kind` on n_wg workgroups, each wave looping iters times. */
 int fa_probe(int kind, int64_t n_wg, int64_t iters, float *sink, uint64_t *clocks, void *stream);
+
+/* Streaming read of bytes of buf by n_wg workgroups (see above). */
+int fa_probe_hbm_read(const void *buf, int64_t bytes, int64_t n_wg, float *sink, void *stream);
 
 /*
  * Work of one loop iteration of one wave: FLOPs for the MFMA probes (2 per

@@ -53,6 +53,15 @@ def test_probe_host_side():
     assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, None) == fa.FA_ERR_NULL
     assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, 0x1002) == fa.FA_ERR_ALIGN
     assert fa.fa_probe(fa.FA_PROBE_EXP, 1, 1, 0x1000, 0x2004) == fa.FA_ERR_ALIGN
+    # the HBM read probe: byte count, grid, pointers and alignment
+    assert fa.fa_probe_hbm_read(0x10000, 0, 1, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe_hbm_read(0x10000, 24, 1, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe_hbm_read(0x10000, 16, 0, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe_hbm_read(0x10000, 16, (1 << 20) + 1, 0x1000) == fa.FA_ERR_SHAPE
+    assert fa.fa_probe_hbm_read(None, 16, 1, 0x1000) == fa.FA_ERR_NULL
+    assert fa.fa_probe_hbm_read(0x10000, 16, 1, None) == fa.FA_ERR_NULL
+    assert fa.fa_probe_hbm_read(0x10008, 16, 1, 0x1000) == fa.FA_ERR_ALIGN
+    assert fa.fa_probe_hbm_read(0x10000, 16, 1, 0x1002) == fa.FA_ERR_ALIGN
 
 
 def test_args_struct_layout(tmp_path):

@@ -34,3 +34,25 @@ def test_probe_runs(kind):
     assert fa.fa_probe(kind, n_wg, iters, sink.data_ptr(), None, None) == fa.FA_OK
     torch.cuda.synchronize()
     assert not math.isnan(float(sink[0]))
+
+
+def test_hbm_read_probe_reads_every_chunk():
+    """Thread t of T reads 16-byte chunks t, t + T, ...: with a zero buffer
+    every sink value is 0; a word planted in chunk c shows up (low 16 bits)
+    in thread c mod T only, for the first chunk, one in the unrolled loop and
+    the last (tail) chunk."""
+    n_wg, nbytes = 3, 16 * (3 * 256 * 8 * 2 + 77)
+    T = n_wg * 256
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.full((T,), float("nan"), device="cuda")
+    assert fa.fa_probe_hbm_read(buf.data_ptr(), nbytes, n_wg, sink.data_ptr(), None) == fa.FA_OK
+    torch.cuda.synchronize()
+    assert bool((sink == 0).all())
+    for c in (0, 5 * T + 17, nbytes // 16 - 1):
+        buf.zero_()
+        buf[4 * c + 2] = 0x1234_ABCD
+        assert fa.fa_probe_hbm_read(buf.data_ptr(), nbytes, n_wg, sink.data_ptr(), None) == fa.FA_OK
+        torch.cuda.synchronize()
+        want = torch.zeros(T, device="cuda")
+        want[c % T] = float(0xABCD)
+        assert torch.equal(sink, want), c
