@@ -507,9 +507,9 @@ int launch_merge(int dtype, int d, const KParams &p, void *stream) {
 // Host-side table of the compiled 16-bit variants.
 const Variant *variants16(int *count) {
     static const Variant table[] = {
-        // default first: d = 64 runs two 4-wave workgroups per CU (measured
-        // 5-10 % faster than one 8-wave workgroup on B=64 H=16 N=1024 and on
-        // causal N=4096, equal at longer N)
+        // default first: d = 64 runs 4-wave workgroups, three per CU
+        // (measured 7-13 % faster than 8-wave workgroups on B=64 H=16
+        // N=1024 and on causal N from 4096 to 65536)
         FA_V16(__bf16, FA_BF16, 64, 4, 64, 0),
         FA_V16(__bf16, FA_BF16, 64, 8, 128, 0),
         FA_V16(__bf16, FA_BF16, 64, 8, 64, 0),
