@@ -89,6 +89,19 @@ def test_bwd_random_shapes(idx):
     say(errs)
     assert_grads_within(errs, str(RANDOM[idx]))
 
+@pytest.mark.parametrize("d,dt,causal", [(64, "bf16", True), (128, "f16", False)])
+def test_bwd_many_tiny_heads(d, dt, causal):
+    """61 x 67 = 4087 (batch, head) slices of 5 queries and 9 keys: grids of
+    dQ and dK/dV workgroups that are not multiples of the 8 XCDs."""
+    w, x = random_problem(910 + d, 61, 67, 5, 9, d, dt, causal)
+    dout = make_dout(w)
+    dq, dk, dv = run_bwd(w, x, dout)
+    rq, rk, rv = oracle.backward(x["q"], x["k"], x["v"], dout, w.sm_scale, causal)
+    errs = {"dQ": grad_errors(to64(dq), rq), "dK": grad_errors(to64(dk), rk), "dV": grad_errors(to64(dv), rv)}
+    say(errs)
+    assert_grads_within(errs, "many heads")
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
 def test_bwd_scales(scale):
     w, x = random_problem(420, 1, 2, 150, 190, 64, "bf16", True, scale=scale)

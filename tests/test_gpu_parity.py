@@ -84,6 +84,17 @@ def test_random_shapes_match_oracle(idx):
     say(err)
     assert_within(w, err)
 
+@pytest.mark.parametrize("d,dt,causal", [(64, "bf16", False), (128, "f16", True), (128, "fp8_e4m3", False)])
+def test_many_tiny_heads(d, dt, causal):
+    """67 x 131 = 8777 (batch, head) slices of 5 queries and 7 keys: one
+    workgroup per slice, a grid that is not a multiple of the 8 XCDs, so the
+    workgroup-id remapping runs over its whole range and its tail."""
+    w, x = random_problem(900 + d, 67, 131, 5, 7, d, dt, causal)
+    err = full_parity(w, x=x)
+    say(err)
+    assert_within(w, err)
+
+
 def test_single_head_f32_workload():
     """The 1x1x256x64 float32 workload, whole tensor."""
     w = WORKLOADS["single_head_f32_n256_d64"]
