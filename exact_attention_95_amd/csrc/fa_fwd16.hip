@@ -53,8 +53,9 @@ struct Cfg {
     // waves per SIMD the register budget must allow: workgroups of 4 waves
     // with d <= 128 run two per CU (the split kernels are bound by HBM and
     // want them in flight; at d = 64 the two workgroups' waves on a SIMD
-    // are not tied by one barrier and overlap each other's softmax)
-    static constexpr int MIN_WAVES = (SPLIT_ || (NW_ == 4 && D_ <= 128)) ? 2 : 1;
+    // are not tied by one barrier and overlap each other's softmax).  At
+    // d = 256 every kernel, split or not, needs one SIMD's registers per wave.
+    static constexpr int MIN_WAVES = ((SPLIT_ || NW_ == 4) && D_ <= 128) ? 2 : 1;
     static constexpr bool CAUSAL = CAUSAL_;
     static constexpr int RB = D * 2;                      // LDS / global row bytes
     static constexpr int NC = RB / 16;                    // 16-byte chunks per row
@@ -501,6 +502,8 @@ int launch_merge(int dtype, int d, const KParams &p, void *stream) {
     if (dtype == FA_BF16 && d == 128) return launch_merge_t<__bf16, 128>(p, stream);
     if (dtype == FA_F16 && d == 64) return launch_merge_t<_Float16, 64>(p, stream);
     if (dtype == FA_F16 && d == 128) return launch_merge_t<_Float16, 128>(p, stream);
+    if (dtype == FA_BF16 && d == 256) return launch_merge_t<__bf16, 256>(p, stream);
+    if (dtype == FA_F16 && d == 256) return launch_merge_t<_Float16, 256>(p, stream);
     return 1;
 }
 
@@ -539,6 +542,10 @@ const Variant *variants16(int *count) {
         FA_V16S(_Float16, FA_F16, 64, 4, 64, 1),
         FA_V16S(_Float16, FA_F16, 128, 4, 64, 0),
         FA_V16S(_Float16, FA_F16, 128, 4, 64, 1),
+        FA_V16S(__bf16, FA_BF16, 256, 4, 32, 0),
+        FA_V16S(__bf16, FA_BF16, 256, 4, 32, 1),
+        FA_V16S(_Float16, FA_F16, 256, 4, 32, 0),
+        FA_V16S(_Float16, FA_F16, 256, 4, 32, 1),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -324,7 +324,7 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None,
 def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int = 0,
                 out=None, lse=None, with_lse: bool = True, stream=None, tile: int = 0,
                 workspace=None, noalloc: bool = False):
-    """Split-KV attention forward (bf16/fp16, d in {64, 128}); returns (O, LSE).
+    """Split-KV attention forward (bf16/fp16, d in {64, 128, 256}); returns (O, LSE).
 
     Same contract as ``fwd``; the key range is processed in ``num_splits``
     chunks (0: library choice) whose partials are merged on the GPU.  The

@@ -272,7 +272,8 @@ def test_splitkv_workspace_bytes():
     assert fa.fa_splitkv_workspace_bytes(a, 1000) > 0           # capped at one chunk per tile
     assert fa.fa_splitkv_workspace_bytes(a, 0) > 0
     assert fa.fa_splitkv_workspace_bytes(a, -1) == -1
-    assert fa.fa_splitkv_workspace_bytes(good_args(d=256), 0) == -1
+    # d = 256: 90 keys make 2 tiles, one chunk; 600 rows of 256 floats and their LSE
+    assert fa.fa_splitkv_workspace_bytes(good_args(d=256), 0) == 600 * 256 * 4 + -(-600 * 4 // 256) * 256
     assert fa.fa_splitkv_workspace_bytes(good_args(dtype=fa.FA_F32), 0) == -1
     assert fa.fa_splitkv_workspace_bytes(good_args(B=0), 0) == 0
     assert fa.fa_fwd_splitkv(good_args(B=0), 0, None, 0) == fa.FA_OK
@@ -459,7 +460,7 @@ def test_noalloc_entry_point_host_checks():
     assert lib.fa_fwd_splitkv_noalloc(None, 0) == fa.FA_ERR_NULL
     assert fa.fa_fwd_splitkv_noalloc(good_args(B=0), 0) == fa.FA_OK
     assert fa.fa_fwd_splitkv_noalloc(good_args(d=96), 0) == fa.FA_ERR_HEAD_DIM
-    assert fa.fa_fwd_splitkv_noalloc(good_args(d=256), 0) == fa.FA_ERR_VARIANT
+    assert fa.fa_fwd_splitkv_noalloc(good_args(dtype=fa.FA_F32), 0) == fa.FA_ERR_VARIANT
     assert fa.fa_fwd_splitkv_noalloc(good_args(), -1) == fa.FA_ERR_SHAPE
     assert fa.fa_fwd_splitkv_noalloc(good_args(dropout_p=0.2), 0) == fa.FA_ERR_DROPOUT
     # 64 heads of 4096 rows at d = 128: one chunk, 128 MiB of partials

@@ -32,6 +32,11 @@ CASES = [
     (1, 2, 1, 70001, 128, "bf16", False, 0),
     (1, 1, 1, 100, 64, "f16", False, 1000),
     (3, 1, 1, 129, 128, "f16", False, 2),
+    # d = 256 (32-key tiles inside the 64-key chunks)
+    (2, 2, 1, 5000, 256, "bf16", False, 0),
+    (1, 2, 37, 3001, 256, "f16", True, 3),
+    (1, 1, 1, 33, 256, "bf16", False, 1000),
+    (1, 2, 130, 700, 256, "bf16", True, 4),
 ]
 
 
