@@ -350,7 +350,7 @@ extern "C" int fa_fwd_splitkv(const fa_fwd_args *a, int num_splits, void *worksp
     p.n_qblk = (int)((a->N_q + v->br - 1) / v->br);
     p.n_wg = n_split * p.n_bh * p.n_qblk;
     p.c = fmaxf((float)score_factor(a), FLT_MIN);
-    p.o_mul = 1.0f;
+    p.o_mul = a->dtype == FA_FP8_E4M3 ? a->descale_v : 1.0f;  // applied by the merge
     p.neg = a->scale < 0 ? 1 : 0;
     p.n_split = n_split;
     p.kv_split = kv_split;

@@ -503,6 +503,7 @@ int launch_merge(int dtype, int d, const KParams &p, void *stream) {
     if (dtype == FA_F16 && d == 64) return launch_merge_t<_Float16, 64>(p, stream);
     if (dtype == FA_F16 && d == 128) return launch_merge_t<_Float16, 128>(p, stream);
     if (dtype == FA_BF16 && d == 256) return launch_merge_t<__bf16, 256>(p, stream);
+    if (dtype == FA_FP8_E4M3 && d == 128) return launch_merge_t<__bf16, 128>(p, stream);  // bf16 O
     if (dtype == FA_F16 && d == 256) return launch_merge_t<_Float16, 256>(p, stream);
     return 1;
 }

@@ -35,12 +35,19 @@
 namespace fa {
 namespace {
 
-template <bool CAUSAL_>
+// SPLIT: the workgroup covers one chunk of the key range (split-KV, with
+// 4 waves) and writes a float32 partial output and LSE instead of O.
+template <bool CAUSAL_, bool SPLIT_ = false, int NW_ = 8>
 struct Cfg8 {
-    static constexpr int D = 128, NW = 8, BC = 64, NT = NW * 64, BR = 32 * NW;
-    static constexpr bool CAUSAL = CAUSAL_;
+    static constexpr int D = 128, NW = NW_, BC = 64, NT = NW * 64, BR = 32 * NW;
+    static constexpr bool CAUSAL = CAUSAL_, SPLIT = SPLIT_;
     static constexpr int RB = D;            // bytes per row
     static constexpr int TILE = BC * RB;    // 8 KB
+    static constexpr int LDI = TILE / (1024 * NW);  // copy instructions per wave per tile
+    // waves per SIMD the register budget must allow: two workgroups of 4
+    // waves per CU for the split kernels (bound by HBM, they want copies in
+    // flight), one of 8 waves otherwise
+    static constexpr int MIN_WAVES = NW_ == 4 ? 2 : 1;
     static constexpr int LDS = 4 * TILE;    // K0, K1, V0, V1
     static constexpr int KS = D / 64;       // k-steps of S^T = K Q^T
     static constexpr int KB = BC / 32;
@@ -49,7 +56,7 @@ struct Cfg8 {
     // stored as 2^PSHIFT P, at most 2^(TAU + PSHIFT) = 256 < 448 (E4M3's max)
     static constexpr float TAU = 2.0f, PSHIFT = 6.0f;
     static_assert(TAU + PSHIFT <= 8.0f, "scaled P must stay below E4M3's largest value");
-    static_assert(TILE == 1024 * NW, "one copy instruction per wave per tile");
+    static_assert(TILE % (1024 * NW) == 0, "whole copy instructions per wave per tile");
 };
 
 // Key row of S^T MFMA row rho (within a 32-key block).
@@ -63,15 +70,18 @@ __device__ __forceinline__ int kswz8(int r) { return ((r >> 1) & 3) | (((r >> 4)
 __device__ __forceinline__ int vswz8(int r) { return 2 * ((r >> 1) & 3); }
 
 // Issues the direct-to-LDS copy of rows [t0, t0 + BC) of one head (one 16-byte
-// chunk per lane, one instruction per wave); rows past n_kv are clamped.
+// chunk per lane, LDI instructions per wave); rows past n_kv are clamped.
 template <class C, bool IS_V>
 __device__ __forceinline__ void copy_tile(const char *src, int t0, int n_kv, char *buf, int w, int lane) {
-    const int chunk = w * 64 + lane;
-    const int r = chunk >> 3;
-    const int pc = chunk & 7;
-    const int gr = min(t0 + r, n_kv - 1);
-    const int lc = pc ^ (IS_V ? vswz8(r) : kswz8(r));
-    copy16_to_lds(src + (int64_t)gr * C::RB + 16 * lc, buf + w * 1024);
+#pragma unroll
+    for (int i = 0; i < C::LDI; ++i) {
+        const int chunk = (i * C::NW + w) * 64 + lane;
+        const int r = chunk >> 3;
+        const int pc = chunk & 7;
+        const int gr = min(t0 + r, n_kv - 1);
+        const int lc = pc ^ (IS_V ? vswz8(r) : kswz8(r));
+        copy16_to_lds(src + (int64_t)gr * C::RB + 16 * lc, buf + (i * C::NW + w) * 1024);
+    }
 }
 
 __device__ __forceinline__ void both_halves8(float x, float &lo, float &hi) {
@@ -196,7 +206,7 @@ __device__ __forceinline__ void softmax8_tail(const f32x16 &s1, i32x8 &pb, float
 }
 
 template <class C>
-__global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
+__global__ __launch_bounds__(C::NT, C::MIN_WAVES) void fwd8_kernel(KParams p) {
     // K and V buffers as four LDS objects: a read of one is not held up by a
     // copy in flight into another
     __shared__ __attribute__((aligned(1024))) char sk0[C::TILE];
@@ -211,24 +221,41 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    const int bid = xcd_remap(blockIdx.x, p.n_wg);
+    int bid = xcd_remap(blockIdx.x, p.n_wg);
+    int split = 0;
+    if (C::SPLIT) {
+        const int per = p.n_bh * p.n_qblk;
+        split = bid / per;
+        bid -= split * per;
+    }
     const int bh = bid / p.n_qblk;
     int qb = bid - bh * p.n_qblk;
     if (C::CAUSAL) qb = p.n_qblk - 1 - qb;
     const int q0 = qb * C::BR;
     const int wq0 = q0 + w * 32;
     const int qi = wq0 + l32;
-    const int n_q = p.n_q, n_kv = p.n_kv;
+    const int n_q = p.n_q;
+    // Keys [kofs, kofs + n_kv) of the head; the causal comparisons below use
+    // query indices shifted by -kofs so that they stay relative to this range.
+    const int kofs = C::SPLIT ? split * p.kv_split : 0;
+    const int n_kv = C::SPLIT ? min(p.kv_split, p.n_kv - kofs) : p.n_kv;
+    const int rwq0 = wq0 - kofs, rqi = qi - kofs;
     const char *qh = p.q + (int64_t)bh * n_q * C::RB;
-    const char *kh = p.k + (int64_t)bh * n_kv * C::RB;
-    const char *vh = p.v + (int64_t)bh * n_kv * C::RB;
+    const char *kh = p.k + ((int64_t)bh * p.n_kv + kofs) * C::RB;
+    const char *vh = p.v + ((int64_t)bh * p.n_kv + kofs) * C::RB;
 
     int ntile = (n_kv + C::BC - 1) / C::BC;
-    if (C::CAUSAL) ntile = min(ntile, min(q0 + C::BR - 1, n_q - 1) / C::BC + 1);
+    if (C::CAUSAL) {
+        const int last = min(q0 + C::BR - 1, n_q - 1) - kofs;  // last row, relative
+        ntile = last < 0 ? 0 : min(ntile, last / C::BC + 1);
+    }
     int wn = 0;
-    if (wq0 < n_q) wn = C::CAUSAL ? min(ntile, min(wq0 + 31, n_q - 1) / C::BC + 1) : ntile;
+    if (wq0 < n_q) {
+        const int last = min(wq0 + 31, n_q - 1) - kofs;
+        wn = !C::CAUSAL ? ntile : (last < 0 ? 0 : min(ntile, last / C::BC + 1));
+    }
     auto need_mask = [&](int t) {
-        return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > wq0);
+        return (t + 1) * C::BC > n_kv || (C::CAUSAL && (t + 1) * C::BC - 1 > rwq0);
     };
 
     copy_tile<C, false>(kh, 0, n_kv, kbuf(0), w, lane);
@@ -287,7 +314,7 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
     if (wn > 0) {
         f32x16 s[C::KB];
         qk8<C>(s, kbuf(0), koff, qf);
-        if (need_mask(0)) mask8<C>(s, 0, qi, n_kv, h);
+        if (need_mask(0)) mask8<C>(s, 0, rqi, n_kv, h);
         softmax8_head<C>(s, p0, m_use, l_acc, alpha, raised, c, bias_tail);
         s_tail = s[1];
         raised = false;
@@ -312,7 +339,7 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
             // keep the tail under the S MFMAs: without this the compiler
             // sinks it past the masking branch, next to the PV MFMAs
             asm volatile("" : "+v"(pc), "+v"(l_acc));
-            if (masked) mask8<C>(s, (t + 1) * C::BC, qi, n_kv, h);
+            if (masked) mask8<C>(s, (t + 1) * C::BC, rqi, n_kv, h);
             pv8<C>(o, vbuf(PAR), voff, pc);
             softmax8_head<C>(s, pn, m_use, l_acc, alpha, raised, c, bias_tail);
             s_tail = s[1];
@@ -335,12 +362,32 @@ __global__ __launch_bounds__(C::NT) void fwd8_kernel(KParams p) {
     // bytes use the swizzle (r / 2) % 8 of their 16-byte chunks, which keeps
     // the 8-byte writes by column and the 16-byte reads by row free of bank
     // conflicts.
-    static_assert(C::TILE == 2 * 4096 && C::NW == 8, "two waves' staging per tile buffer");
-    __syncthreads();
-    if (wq0 >= n_q) return;
     float lo, hi;
     both_halves8(l_acc, lo, hi);
     const float l_tot = lo + hi;
+    if (C::SPLIT) {
+        // partial of this key chunk, float32 and not yet multiplied by the V
+        // descale (the merge applies it); a row that sees no key of the chunk
+        // (causal) gets O = 0 and LSE = -inf, i.e. weight 0 in the merge
+        if (qi >= n_q) return;
+        const int64_t row = ((int64_t)split * p.n_bh + bh) * n_q + qi;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float *orow = p.part_o + row * C::D;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = o[db][4 * jj + e] * inv;
+                *(f32x4 *)(orow + 32 * db + 8 * jj + 4 * h) = out;
+            }
+        if (h == 0) p.part_lse[row] = l_tot > 0.f ? (m_use - C::PSHIFT + __log2f(l_tot)) * kLn2 : kNegInf;
+        return;
+    }
+    static_assert(C::SPLIT || (C::TILE == 2 * 4096 && C::NW == 8), "two waves' staging per tile buffer");
+    __syncthreads();
+    if (wq0 >= n_q) return;
     const float inv = p.o_mul / l_tot;
     char *stage = (w < 2 ? sk0 : w < 4 ? sk1 : w < 6 ? sv0 : sv1) + 4096 * (w & 1);
     const int rr = lane >> 3, cc = lane & 7;
@@ -379,6 +426,8 @@ const Variant *variants8(int *count) {
     static const Variant table[] = {
         Variant{FA_FP8_E4M3, 128, 0, 0, 256, "br8x32_bc64", &launch8<Cfg8<false>>},
         Variant{FA_FP8_E4M3, 128, 1, 0, 256, "br8x32_bc64", &launch8<Cfg8<true>>},
+        Variant{FA_FP8_E4M3, 128, 0, 1, 128, "split_br4x32_bc64", &launch8<Cfg8<false, true, 4>>},
+        Variant{FA_FP8_E4M3, 128, 1, 1, 128, "split_br4x32_bc64", &launch8<Cfg8<true, true, 4>>},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -323,10 +323,11 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, descale=None,
 
 def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int = 0,
                 out=None, lse=None, with_lse: bool = True, stream=None, tile: int = 0,
-                workspace=None, noalloc: bool = False):
-    """Split-KV attention forward (bf16/fp16, d in {64, 128, 256}); returns (O, LSE).
+                workspace=None, noalloc: bool = False, descale=None):
+    """Split-KV attention forward (bf16/fp16 with d in {64, 128, 256}, or
+    float8_e4m3fn with d = 128 and bf16 O); returns (O, LSE).
 
-    Same contract as ``fwd``; the key range is processed in ``num_splits``
+    Same contract as ``fwd`` (``descale`` as there); the key range is processed in ``num_splits``
     chunks (0: library choice) whose partials are merged on the GPU.  The
     float32 workspace is allocated with torch unless ``workspace`` (a uint8
     device tensor) is given, or unless ``noalloc``: then the partials go to
@@ -334,16 +335,17 @@ def fwd_splitkv(q, k, v, scale: float | None = None, causal: bool = False, num_s
     """
     import torch
     # an unsupported (but consistent) dtype is the C library's to report
-    check_tensors(q, k, v, out, lse, workspace=workspace, out_dtype=q.dtype)
+    out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    check_tensors(q, k, v, out, lse, workspace=workspace, out_dtype=out_dtype)
     B, H, N_q, d = q.shape
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
-        out = torch.empty((B, H, N_q, d), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, N_q, d), dtype=out_dtype, device=q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
     stream = _stream_handle(stream, q.device)
-    args = make_args(q, k, v, out, lse, scale, causal, (1.0, 1.0, 1.0), stream, tile)
+    args = make_args(q, k, v, out, lse, scale, causal, descale or (1.0, 1.0, 1.0), stream, tile)
     if noalloc:
         if workspace is not None:
             raise ValueError("noalloc takes no workspace")

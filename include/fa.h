@@ -171,8 +171,9 @@ int fa_validate(const fa_fwd_args *args);
  * the GPU (few query rows, long key ranges).
  *
  * args: as for fa_fwd_ex, except that N_kv may exceed
- * FA_MAX_NKV_SINGLE_PASS (up to 2^30); dtype FA_BF16 or FA_F16 and d in
- * {64, 128, 256} (otherwise FA_ERR_VARIANT); tile_override 0 or 1.  num_splits:
+ * FA_MAX_NKV_SINGLE_PASS (up to 2^30); dtype FA_BF16 or FA_F16 with d in
+ * {64, 128, 256}, or FA_FP8_E4M3 with d = 128 (descales as for fa_fwd_ex,
+ * bf16 O) (otherwise FA_ERR_VARIANT); tile_override 0 or 1.  num_splits:
  * 0 lets the library choose, otherwise an upper bound (every chunk is
  * non-empty, so fewer may be used), except that no chunk is made longer
  * than FA_MAX_NKV_SINGLE_PASS keys: more chunks are used where needed.
