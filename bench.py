@@ -594,6 +594,7 @@ OTHER_WORKLOADS = [("single_head_f32_n256_d64", "fwd"), ("gpt2_medium_bf16_n1024
                    ("long_f16_causal_n65536_d64", "fwd"), ("headline_bf16_n8192_d128", "fwd"),
                    ("headline_bf16_causal_n8192_d128", "fwd"), ("large_head_bf16_n16384_d256", "fwd"),
                    ("fp8_e4m3_n16384_d128", "fwd"), ("decode_bf16_b8_h32_nkv65536_d128", "splitkv"),
+                   ("decode_e4m3_b8_h32_nkv65536_d128", "splitkv"),
                    ("headline_bf16_n8192_d128", "bwd"), ("large_head_bf16_n16384_d256", "bwd")]
 
 

@@ -82,6 +82,8 @@ WORKLOADS = {
         Workload("fp8_e4m3_n16384_d128", 6, 2, 16, 16384, 16384, 128, "fp8_e4m3"),
         # decode: one new query row per sequence against a long key/value cache
         Workload("decode_bf16_b8_h32_nkv65536_d128", 7, 8, 32, 1, 65536, 128, "bf16"),
+        # the same decode with an E4M3 key/value cache (per-tensor descales)
+        Workload("decode_e4m3_b8_h32_nkv65536_d128", 8, 8, 32, 1, 65536, 128, "fp8_e4m3"),
     ]
 }
 

@@ -42,7 +42,8 @@ CASES = [
 
 def run_split(w, x, num_splits):
     q, k, v = (x[n].cuda() for n in ("q", "k", "v"))
-    o, lse = fa.fwd_splitkv(q, k, v, scale=w.sm_scale, causal=w.causal, num_splits=num_splits)
+    o, lse = fa.fwd_splitkv(q, k, v, scale=w.sm_scale, causal=w.causal, num_splits=num_splits,
+                            descale=x["descale"])
     torch.cuda.synchronize()
     return o, lse
 
@@ -111,9 +112,12 @@ def test_splitkv_errors():
     assert fa.fa_fwd_splitkv(a32, 0, ws.data_ptr(), need) == fa.FA_ERR_VARIANT
 
 
-def test_decode_workload_sampled_heads():
-    """Full-size decode (B=8, H=32, N_kv=65536, d=128): every row of 8 heads."""
-    w = WORKLOADS["decode_bf16_b8_h32_nkv65536_d128"]
+@pytest.mark.parametrize("name", ["decode_bf16_b8_h32_nkv65536_d128", "decode_e4m3_b8_h32_nkv65536_d128"])
+def test_decode_workload_sampled_heads(name):
+    """Full-size decode (B=8, H=32, N_kv=65536, d=128; bf16, or E4M3 with
+    per-tensor descales against the oracle on the decoded operands): every
+    row of 8 heads."""
+    w = WORKLOADS[name]
     x = make_inputs(w)
     o, lse = run_split(w, x, 0)
     rng = np.random.default_rng(5)
@@ -121,7 +125,8 @@ def test_decode_workload_sampled_heads():
     o_s = o.reshape(-1, w.d)[torch.from_numpy(rows).cuda()].double().cpu().numpy()
     l_s = lse.reshape(-1)[torch.from_numpy(rows).cuda()].double().cpu().numpy()
     del o, lse
-    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.sm_scale, False, rows=rows)
+    qo, ko, vo = oracle_operands(w, x)
+    o_ref, lse_ref = oracle.attention(qo, ko, vo, w.sm_scale, False, rows=rows)
     err = errors(o_s, l_s, o_ref, lse_ref)
     say(err)
     assert_within(w, err, "decode sampled")
