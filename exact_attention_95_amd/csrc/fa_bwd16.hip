@@ -5,7 +5,7 @@
 // scores and probabilities tile by tile.  With P_ij = exp(scale q_i.k_j -
 // LSE_i) and the textbook gradients of softmax(scale Q K^T) V,
 //
-//   D_i   = sum_c dO_ic O_ic                      bwd_delta_kernel
+//   D_i   = sum_c dO_ic O_ic                      bwd_dq_kernel, per row first
 //   dQ_i  = scale sum_j P_ij (dP_ij - D_i) k_j     bwd_dq_kernel (query blocks)
 //   dV_j  = sum_i P_ij dO_i                         bwd_dkdv_kernel (key blocks)
 //   dK_j  = scale sum_i P_ij (dP_ij - D_i) q_i
@@ -336,32 +336,6 @@ __device__ __forceinline__ void pv_dq_rolling(f32x16 (&o)[C::QDB], const char *V
 }
 
 // ---------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic (float32), D/8 lanes per row, 8 elements each; the
-// same pass stores LSE_i log2(e), the exponent offset both gradient kernels
-// need per row.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-    typedef T T8 __attribute__((ext_vector_type(8)));
-    constexpr int TPR = D / 8;
-    const int64_t n_rows = (int64_t)p.n_bh * p.n_q;
-    const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-    const int col = (threadIdx.x % TPR) * 8;
-    float acc = 0.f;
-    if (row < n_rows) {
-        const T8 a = __builtin_bit_cast(T8, *(const u32x4 *)(p.o + (row * D + col) * 2));
-        const T8 b = __builtin_bit_cast(T8, *(const u32x4 *)(p.dout + (row * D + col) * 2));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
-    }
-#pragma unroll
-    for (int m = TPR / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m);
-    if (row < n_rows && threadIdx.x % TPR == 0) {
-        p.delta[row] = acc;
-        p.lse2[row] = p.lse[row] * kLog2e;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // dQ: one workgroup per (batch*head, block of 32*NW query rows), streaming
 // K and V tiles of 64 keys.  K is stored in the layout read both ways (by
 // rows and transposed), V in the K-style layout (read by rows only).
@@ -414,8 +388,28 @@ __global__ __launch_bounds__(C::NT, C::MIN_WAVES) void bwd_dq_kernel(BwdParams p
     load_rows<C>(qh, qi, n_q, qf, h);
     load_rows<C>(gh, qi, n_q, gf, h);
     const int64_t row = (int64_t)bh * n_q + (qi < n_q ? qi : n_q - 1);
-    const float lse2 = p.lse2[row];
-    const float dlt = p.delta[row];
+    // D_i = sum_c dO_ic O_ic (float32) and LSE_i log2 e of this lane's row,
+    // for this kernel and, through the workspace, for the dK/dV kernel that
+    // runs after it: each lane reads the half of O's row that matches its dO
+    // operand, and the two half-waves' sums are added
+    float dlt;
+    {
+        typedef typename M::v8 v8o;
+        const char *orow = p.o + (row * C::RB) + 16 * h;
+        float acc = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const v8o ov = __builtin_bit_cast(v8o, *(const u32x4 *)(orow + 32 * ks));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gf[ks][e];
+        }
+        dlt = sum_halves(acc);
+    }
+    const float lse2 = p.lse[row] * kLog2e;
+    if (C::PART != 2 && h == 0 && qi < n_q) {  // the second dQ pass finds them stored
+        p.delta[row] = dlt;
+        p.lse2[row] = lse2;
+    }
     const float c = p.c;
     DropQuad dr{};
     if (C::DROP) dr = make_drop_quad(p.p8, (unsigned)qi >> 2, (unsigned)bh, p.drop_off, p.seed_lo, p.seed_hi);
@@ -880,9 +874,6 @@ int launch_bwd_t(const BwdParams &p, void *stream) {
     hipStream_t st = (hipStream_t)stream;
     const int64_t rows = (int64_t)p.n_bh * p.n_q;
     if (rows > 0) {
-        constexpr int RPB = 256 / (D / 8);
-        hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                           st, p);
         const int nq = (p.n_q + CQ::BR - 1) / CQ::BR;
         hipLaunchKernelGGL(bwd_dq_kernel<CQ>, dim3(p.n_bh * nq), dim3(CQ::NT), 0, st, p);
         if constexpr (QSPLIT) hipLaunchKernelGGL(bwd_dq_kernel<CQ2>, dim3(p.n_bh * nq), dim3(CQ2::NT), 0, st, p);
